@@ -1,0 +1,129 @@
+"""Seeded synthetic inputs for the reproducible FP32 matmul workloads.
+
+This module generates operand bytes only and holds none of the matmul's
+arithmetic; the GPU path and the CPU oracle both consume what it returns.
+It imports nothing else from this package.
+
+Recipe (numpy PCG64; seeds A = 1000*c + 1, B = 1000*c + 2 for workload c):
+
+* ``uniform``: ``(integers(0, 2**24) - 2**23) * 2**-23`` -- exact U[-1, 1) on
+  the 2^-23 grid, never subnormal;
+* ``int8grid``: integers uniform in {-8, ..., 8} (every product and partial
+  sum up to K = 2^18 is an integer below 2^24, so the result is exact);
+* ``normal(std)``: float32 ``standard_normal`` times float32 ``std``, then any
+  nonzero |x| < 2^-126 replaced by copysign(2^-126, x) so no input is
+  subnormal (at these sizes it never triggers);
+
+The transformer-shaped workloads are synthetic stand-ins for the
+Llama-3.1-1B and -8B MLP products that the Verde and RepOps article measures
+(section 4.3): random data with the activation (std 1) and weight (std 0.02)
+scales of those layers, since no weights or datasets are used here.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+TINY = np.float32(2.0 ** -126)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    trans_a: bool
+    trans_b: bool
+    a_dist: str
+    b_dist: str
+    seed_a: int
+    seed_b: int
+    description: str
+
+    @property
+    def a_shape(self):
+        """Shape of A as stored (row-major)."""
+        return (self.K, self.M) if self.trans_a else (self.M, self.K)
+
+    @property
+    def b_shape(self):
+        """Shape of B as stored (row-major)."""
+        return (self.N, self.K) if self.trans_b else (self.K, self.N)
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("square256_uniform", 256, 256, 256, False, False, "uniform", "uniform",
+                 1001, 1002, "M=N=K=256, A,B ~ U[-1,1) on the 2^-23 grid"),
+        Workload("square256_int", 256, 256, 256, False, False, "int8grid", "int8grid",
+                 1011, 1012, "M=N=K=256, integer entries in [-8, 8]: exact result"),
+        Workload("square1024_normal", 1024, 1024, 1024, False, False, "normal1", "normal1",
+                 2001, 2002, "M=N=K=1024, A,B ~ N(0,1) float32, no subnormals"),
+        Workload("llama1b_mlp_up", 4096, 8192, 2048, False, False, "normal1", "normal0.02",
+                 3001, 3002, "Llama-3.1-1B-shaped MLP up-projection X W: M=4096 tokens, "
+                 "K=2048, N=8192; X ~ N(0,1), W ~ N(0,0.02)"),
+        Workload("llama8b_mlp_up", 4096, 14336, 4096, False, False, "normal1", "normal0.02",
+                 4001, 4002, "Llama-3.1-8B-shaped MLP up-projection X W: M=4096 tokens, "
+                 "K=4096, N=14336; X ~ N(0,1), W ~ N(0,0.02)"),
+        Workload("llama1b_mlp_dW", 2048, 8192, 4096, True, False, "normal1", "normal1",
+                 5001, 5002, "Llama-3.1-1B MLP weight gradient dW = X^T dY: X stored "
+                 "4096x2048 (transposed operand), dY 4096x8192; K=4096 tokens"),
+        Workload("llama1b_mlp_dX", 4096, 2048, 8192, False, True, "normal1", "normal1",
+                 5002, 5003, "Llama-3.1-1B MLP input gradient dX = dY W^T: dY 4096x8192, "
+                 "W stored 2048x8192 (transposed operand); K=8192"),
+    ]
+}
+
+
+def _draw(dist: str, shape, seed: int) -> np.ndarray:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if dist == "uniform":
+        v = rng.integers(0, 2 ** 24, size=shape, dtype=np.int64) - 2 ** 23
+        return (v.astype(np.float32) * np.float32(2.0 ** -23)).astype(np.float32)
+    if dist == "int8grid":
+        return rng.integers(-8, 9, size=shape, dtype=np.int64).astype(np.float32)
+    if dist.startswith("normal"):
+        std = np.float32(float(dist[len("normal"):]))
+        x = rng.standard_normal(size=shape, dtype=np.float32)
+        if std != np.float32(1.0):
+            x = x * std
+        tiny = (x != 0) & (np.abs(x) < TINY)
+        if tiny.any():
+            x[tiny] = np.copysign(TINY, x[tiny])
+        return x.astype(np.float32, copy=False)
+    raise ValueError("unknown distribution %r" % dist)
+
+
+def make_operands(name: str):
+    """(A, B) as stored, C-contiguous float32, for the named workload."""
+    w = WORKLOADS[name]
+    return _draw(w.a_dist, w.a_shape, w.seed_a), _draw(w.b_dist, w.b_shape, w.seed_b)
+
+
+def random_matrix(shape, seed: int, dist: str = "normal1") -> np.ndarray:
+    """A seeded float32 matrix of any shape with one of the distributions above."""
+    return _draw(dist, shape, seed)
+
+
+def sample_entries(M: int, N: int, count: int, seed: int):
+    """Output coordinates to check at full size: the four corners, the last
+    row and column (ragged tiles), and ``count`` uniform random (i, j)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ii = [0, 0, M - 1, M - 1]
+    jj = [0, N - 1, 0, N - 1]
+    edge = min(64, N)
+    ii += [M - 1] * edge
+    jj += list(rng.integers(0, N, size=edge))
+    edge = min(64, M)
+    ii += list(rng.integers(0, M, size=edge))
+    jj += [N - 1] * edge
+    ii += list(rng.integers(0, M, size=count))
+    jj += list(rng.integers(0, N, size=count))
+    return np.asarray(ii, dtype=np.int64), np.asarray(jj, dtype=np.int64)

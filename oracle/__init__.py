@@ -1,0 +1,151 @@
+"""CPU oracle for the reproducible FP32 matmul -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the CPU-baseline leg of the
+benchmark may import this package.  The GPU library never imports, links or
+calls it, and it imports nothing from the GPU library: the two share no code.
+
+Three independent implementations of one definition (Verde and RepOps
+article, section 3.2 "RepOps design principles", item 2, the matrix
+multiplication example: ``sum = 0``; for k in a fixed order
+``sum = sum + A[i][k] * B[k][j]``; ``C[i][j] = sum``), read as: ascending k,
+the multiply and the add each rounded to binary32 round-to-nearest-even
+(the Zoo chain-soundness spec pins RNE and turns fused multiply-add off),
+gradual underflow, ``sum`` starting at +0.0:
+
+* :func:`matmul_f32` / :func:`entries_f32` -- the plain C triple loop in
+  ``repops_oracle.c`` (the oracle proper), built with gcc;
+* :func:`emulate_f64` -- the same steps in numpy binary64, each result
+  rounded to binary32 (double rounding is innocuous for +, x because
+  53 >= 2*24 + 2; S. A. Figueroa, "When is double rounding innocuous?",
+  1995), vectorised over (i, j);
+* :func:`exact_matmul` -- exact rational arithmetic with a hand-written
+  binary32 round-to-nearest-even rounder; no hardware floating point.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+from .emulate import emulate_f64  # noqa: F401
+from .exact import exact_matmul, round_binary32  # noqa: F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "repops_oracle.c")
+_LIB = os.path.join(_HERE, "librepops_oracle.so")
+
+GCC_FLAGS = [
+    "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math",
+    "-fexcess-precision=standard", "-fPIC", "-shared", "-pthread",
+]
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``repops_oracle.c`` into ``librepops_oracle.so`` with gcc."""
+    global _lib
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", *GCC_FLAGS, "-o", tmp, _SRC], check=True)
+        os.replace(tmp, _LIB)
+        _lib = None
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        i64, fp, ip = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        lib.repops_oracle_matmul_f32.argtypes = [
+            fp, i64, i64, fp, i64, i64, fp, i64, i64, i64, i64, i64, ip, ip, ip]
+        lib.repops_oracle_matmul_f32.restype = ip
+        lib.repops_oracle_entries_f32.argtypes = [
+            fp, i64, i64, fp, i64, i64, i64, i64, i64, ip, ip, fp, fp, i64, fp, ip]
+        lib.repops_oracle_entries_f32.restype = ip
+        lib.repops_oracle_env_status.argtypes = []
+        lib.repops_oracle_env_status.restype = ip
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def env_status() -> int:
+    """0 when the host FP environment is RNE without FTZ/DAZ."""
+    return _load().repops_oracle_env_status()
+
+
+def _operand(x: np.ndarray):
+    """Base pointer and element strides of a float32 array view."""
+    if x.dtype != np.float32:
+        raise TypeError("oracle operands must be float32")
+    if x.ndim != 2:
+        raise ValueError("oracle operands must be 2-D")
+    rs, cs = (s // 4 for s in x.strides)
+    if any(s % 4 for s in x.strides):
+        raise ValueError("strides must be whole elements")
+    return x.ctypes.data, rs, cs
+
+
+def _logical_shapes(A, B, trans_a, trans_b):
+    M, K = (A.shape[1], A.shape[0]) if trans_a else A.shape
+    K2, N = (B.shape[1], B.shape[0]) if trans_b else B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ: %d vs %d" % (K, K2))
+    return M, N, K
+
+
+def matmul_f32(A: np.ndarray, B: np.ndarray, trans_a: bool = False,
+               trans_b: bool = False, nthreads: int | None = None,
+               out: np.ndarray | None = None) -> np.ndarray:
+    """C = op(A) op(B) by the fixed-order definition (the C triple loop).
+
+    ``A``/``B`` are the *stored* matrices, any element strides (negative and
+    zero included); ``trans_*`` are logical transposes.  Returns an M x N
+    float32 array (or fills ``out``).
+    """
+    M, N, K = _logical_shapes(A, B, trans_a, trans_b)
+    if out is None:
+        out = np.empty((M, N), dtype=np.float32)
+    if out.shape != (M, N) or out.dtype != np.float32:
+        raise ValueError("out must be float32 of shape (M, N)")
+    pa, ars, acs = _operand(A)
+    pb, brs, bcs = _operand(B)
+    pc, crs, ccs = _operand(out)
+    rc = _load().repops_oracle_matmul_f32(
+        pa, ars, acs, pb, brs, bcs, pc, crs, ccs, M, N, K,
+        int(bool(trans_a)), int(bool(trans_b)), nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle failed with status %d" % rc)
+    return out
+
+
+def entries_f32(A: np.ndarray, B: np.ndarray, ii, jj, trans_a: bool = False,
+                trans_b: bool = False, nthreads: int | None = None) -> np.ndarray:
+    """C(ii[e], jj[e]) for each e, by the same fixed-order definition."""
+    M, N, K = _logical_shapes(A, B, trans_a, trans_b)
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    if ii.shape != jj.shape or ii.ndim != 1:
+        raise ValueError("ii and jj must be 1-D of equal length")
+    out = np.empty(ii.shape[0], dtype=np.float32)
+    pa, ars, acs = _operand(A)
+    pb, brs, bcs = _operand(B)
+    rc = _load().repops_oracle_entries_f32(
+        pa, ars, acs, pb, brs, bcs, M, N, K, int(bool(trans_a)), int(bool(trans_b)),
+        ii.ctypes.data, jj.ctypes.data, ii.shape[0], out.ctypes.data,
+        nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle failed with status %d" % rc)
+    return out

@@ -1,0 +1,129 @@
+"""Exact-rational brute force for the fixed-order FP32 matmul -- TEST INFRASTRUCTURE ONLY.
+
+No hardware floating point is used for arithmetic: binary32 values are
+decoded from their bits into exact rationals, every multiply and add is done
+exactly with :class:`fractions.Fraction`, and each result is rounded to
+binary32 by :func:`round_binary32`, a hand-written round-to-nearest-even
+(ties to even) rounder with gradual underflow and overflow to infinity, as
+IEEE 754-2008 section 4.3.1 and 7.4 define them.  Signed zeros follow
+IEEE 754-2008 section 6.3: an exact zero sum is +0 under round-to-nearest
+unless both addends are -0; a product's sign is the XOR of the operand signs.
+
+The loop is the definition in the Verde and RepOps article (section 3.2,
+item 2): ``sum = 0``; for k ascending ``sum = sum + a*b``; ``C[i][j] = sum``,
+with the multiply and the add rounded separately.  Intended for tiny shapes.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+QNAN_BITS = 0x7FC00000
+
+# An exact binary32 datum: ("num", sign, magnitude) with magnitude a Fraction
+# >= 0 (sign matters for zero), ("inf", sign, None) or ("nan", 0, None).
+
+
+def decode_binary32(bits: int):
+    sign = (bits >> 31) & 1
+    e = (bits >> 23) & 0xFF
+    m = bits & 0x7FFFFF
+    if e == 0xFF:
+        return ("nan", 0, None) if m else ("inf", sign, None)
+    if e == 0:
+        mag = Fraction(m, 1 << 149)  # subnormal: m * 2^-149
+    else:
+        mag = Fraction((1 << 23) | m) * (Fraction(2) ** (e - 150))
+    return ("num", sign, mag)
+
+
+def round_binary32(sign: int, mag: Fraction) -> int:
+    """Bits of the binary32 nearest to (-1)^sign * mag, ties to even."""
+    if mag == 0:
+        return sign << 31
+    # 2^e <= mag < 2^(e+1)
+    e = mag.numerator.bit_length() - mag.denominator.bit_length()
+    if mag < Fraction(2) ** e:
+        e -= 1
+    q_exp = -149 if e < -126 else e - 23  # quantum of the binade (or subnormals)
+    q = mag / (Fraction(2) ** q_exp)
+    n = q.numerator // q.denominator
+    rem = q - n
+    half = Fraction(1, 2)
+    if rem > half or (rem == half and n % 2 == 1):
+        n += 1
+    if n == 0:  # underflow to zero keeps the sign
+        return sign << 31
+    if n >= (1 << 24):  # carry into the next binade
+        n >>= 1
+        q_exp += 1
+    if n < (1 << 23):  # only possible at q_exp == -149: subnormal
+        return (sign << 31) | n
+    biased = q_exp + 150
+    if biased >= 0xFF:
+        return (sign << 31) | 0x7F800000
+    return (sign << 31) | (biased << 23) | (n - (1 << 23))
+
+
+def exact_mul(x, y):
+    if x[0] == "nan" or y[0] == "nan":
+        return ("nan", 0, None)
+    s = x[1] ^ y[1]
+    if x[0] == "inf" or y[0] == "inf":
+        other = y if x[0] == "inf" else x
+        if other[0] == "num" and other[2] == 0:
+            return ("nan", 0, None)  # inf * 0
+        return ("inf", s, None)
+    return decode_binary32(round_binary32(s, x[2] * y[2]))
+
+
+def exact_add(x, y):
+    if x[0] == "nan" or y[0] == "nan":
+        return ("nan", 0, None)
+    if x[0] == "inf" and y[0] == "inf":
+        return ("inf", x[1], None) if x[1] == y[1] else ("nan", 0, None)
+    if x[0] == "inf":
+        return x
+    if y[0] == "inf":
+        return y
+    vx = -x[2] if x[1] else x[2]
+    vy = -y[2] if y[1] else y[2]
+    v = vx + vy
+    if v == 0:
+        s = 1 if (x[1] == 1 and y[1] == 1 and x[2] == 0 and y[2] == 0) else 0
+        return ("num", s, Fraction(0))
+    return decode_binary32(round_binary32(1 if v < 0 else 0, abs(v)))
+
+
+def encode(x) -> int:
+    if x[0] == "nan":
+        return QNAN_BITS
+    if x[0] == "inf":
+        return (x[1] << 31) | 0x7F800000
+    return round_binary32(x[1], x[2])  # already representable: exact
+
+
+def exact_matmul(A: np.ndarray, B: np.ndarray, trans_a: bool = False,
+                 trans_b: bool = False) -> np.ndarray:
+    """Fixed-order product by exact arithmetic; returns float32 (M, N)."""
+    opA = np.asarray(A, dtype=np.float32)
+    opB = np.asarray(B, dtype=np.float32)
+    opA = opA.T if trans_a else opA
+    opB = opB.T if trans_b else opB
+    M, K = opA.shape
+    K2, N = opB.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    abits = np.ascontiguousarray(opA).view(np.uint32)
+    bbits = np.ascontiguousarray(opB).view(np.uint32)
+    a = [[decode_binary32(int(abits[i, k])) for k in range(K)] for i in range(M)]
+    b = [[decode_binary32(int(bbits[k, j])) for j in range(N)] for k in range(K)]
+    out = np.empty((M, N), dtype=np.uint32)
+    for i in range(M):
+        for j in range(N):
+            s = ("num", 0, Fraction(0))  # sum = +0
+            for k in range(K):
+                s = exact_add(s, exact_mul(a[i][k], b[k][j]))
+            out[i, j] = encode(s)
+    return out.view(np.float32)

@@ -1,0 +1,185 @@
+/*
+ * repops_oracle.c -- plain, slow CPU oracle for the reproducible FP32 matmul.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may load, link or
+ * call this file: it exists so that tests, the smoke check and the CPU
+ * baseline leg of the benchmark can compare the GPU library against an
+ * obviously correct definition.  It shares no code, header or constant with
+ * the GPU library.
+ *
+ * What it computes (Verde and RepOps article, section 3.2 "RepOps design
+ * principles", item 2, the matrix-multiplication example):
+ *
+ *   for every (i, j), in any order:
+ *       sum = +0
+ *       for k = 0, 1, ..., K-1 (this order and no other):
+ *           a = op(A)(i, k);  b = op(B)(k, j)
+ *           sum = sum + a * b
+ *       C(i, j) = sum
+ *
+ * Readings taken here where the pages are open:
+ *   - the multiply and the add are two separately rounded binary32
+ *     operations: the Zoo chain-soundness spec ("Detailed proof:
+ *     deterministic ordering", paragraph "Determinism of left-fold") pins
+ *     round-to-nearest-even and switches fused multiply-add off in
+ *     deterministic mode;
+ *   - IEEE-754 binary32 with gradual underflow (the RepOps article, section
+ *     3.3, requires IEEE-754 compliant hardware), so no flush-to-zero and no
+ *     denormals-are-zero;
+ *   - "sum = 0" is +0.0f and the first product is added to it;
+ *   - op(A)(i,k) = A[i*a_rs + k*a_cs] when trans_a == 0, else
+ *     A[k*a_rs + i*a_cs]; op(B)(k,j) likewise with trans_b.  Strides are in
+ *     elements and describe the stored matrix (the article, section 3.1,
+ *     names tensor strides as a source of nondeterminism: here they only
+ *     change where a value is read from, never the arithmetic).
+ *
+ * Threads split the i loop statically.  i is a free dimension, so the thread
+ * count never changes a bit of the output.
+ *
+ * Build: gcc -std=c11 -O2 -ffp-contract=off -fno-fast-math
+ *        -fexcess-precision=standard -fPIC -shared -pthread
+ */
+#define _GNU_SOURCE
+#include <fenv.h>
+#include <float.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <xmmintrin.h>
+
+#if !defined(FLT_EVAL_METHOD) || FLT_EVAL_METHOD != 0
+#error "binary32 expressions must be evaluated in binary32 (no x87 excess precision)"
+#endif
+
+#pragma STDC FP_CONTRACT OFF
+
+/* Bits of the environment check returned by repops_oracle_env_status(). */
+#define ORACLE_ENV_ROUNDING 1 /* rounding mode is not round-to-nearest-even */
+#define ORACLE_ENV_FTZ 2      /* MXCSR flush-to-zero is on */
+#define ORACLE_ENV_DAZ 4      /* MXCSR denormals-are-zero is on */
+
+int repops_oracle_env_status(void)
+{
+    int bad = 0;
+    unsigned csr = _mm_getcsr();
+    if (fegetround() != FE_TONEAREST) bad |= ORACLE_ENV_ROUNDING;
+    if (csr & (1u << 15)) bad |= ORACLE_ENV_FTZ;
+    if (csr & (1u << 6)) bad |= ORACLE_ENV_DAZ;
+    return bad;
+}
+
+/* One output element, exactly as the definition above reads. */
+static float dot_fixed_order(const float *A, int64_t a_rs, int64_t a_cs, int trans_a,
+                             const float *B, int64_t b_rs, int64_t b_cs, int trans_b,
+                             int64_t i, int64_t j, int64_t K)
+{
+    float sum = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+        const float a = trans_a ? A[k * a_rs + i * a_cs] : A[i * a_rs + k * a_cs];
+        const float b = trans_b ? B[j * b_rs + k * b_cs] : B[k * b_rs + j * b_cs];
+        const float p = a * b;  /* binary32 multiply, rounded on its own */
+        sum = sum + p;          /* binary32 add, rounded on its own */
+    }
+    return sum;
+}
+
+typedef struct {
+    const float *A;
+    int64_t a_rs, a_cs;
+    const float *B;
+    int64_t b_rs, b_cs;
+    float *C;
+    int64_t c_rs, c_cs;
+    int64_t M, N, K;
+    int trans_a, trans_b;
+    /* entries mode: when ii != NULL, compute out[e] for e in [lo, hi) */
+    const int64_t *ii, *jj;
+    float *out;
+    int64_t lo, hi;
+} oracle_job;
+
+static void *run_rows(void *arg)
+{
+    const oracle_job *t = (const oracle_job *)arg;
+    if (t->ii) {
+        for (int64_t e = t->lo; e < t->hi; ++e)
+            t->out[e] = dot_fixed_order(t->A, t->a_rs, t->a_cs, t->trans_a, t->B, t->b_rs,
+                                        t->b_cs, t->trans_b, t->ii[e], t->jj[e], t->K);
+        return NULL;
+    }
+    for (int64_t i = t->lo; i < t->hi; ++i)
+        for (int64_t j = 0; j < t->N; ++j)
+            t->C[i * t->c_rs + j * t->c_cs] =
+                dot_fixed_order(t->A, t->a_rs, t->a_cs, t->trans_a, t->B, t->b_rs, t->b_cs,
+                                t->trans_b, i, j, t->K);
+    return NULL;
+}
+
+/* Split [0, total) statically over nthreads and run each part. */
+static int run_split(oracle_job base, int64_t total, int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((int64_t)nthreads > total) nthreads = (int)(total > 0 ? total : 1);
+    pthread_t tid[256];
+    oracle_job jobs[256];
+    int started = 0, rc = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = base;
+        jobs[t].lo = total * t / nthreads;
+        jobs[t].hi = total * (t + 1) / nthreads;
+    }
+    for (int t = 1; t < nthreads; ++t) {
+        if (pthread_create(&tid[t], NULL, run_rows, &jobs[t]) != 0) {
+            rc = -3;
+            break;
+        }
+        ++started;
+    }
+    run_rows(&jobs[0]);
+    for (int t = 1; t <= started; ++t) pthread_join(tid[t], NULL);
+    if (rc != 0) { /* finish the parts whose threads did not start */
+        for (int t = started + 1; t < nthreads; ++t) run_rows(&jobs[t]);
+    }
+    return 0;
+}
+
+/*
+ * Full product: C(i,j) for all 0 <= i < M, 0 <= j < N, written through
+ * (c_rs, c_cs).  Returns 0, or -1 for negative sizes, -2 for an environment
+ * that is not round-to-nearest-even with gradual underflow.
+ */
+int repops_oracle_matmul_f32(const float *A, int64_t a_rs, int64_t a_cs,
+                             const float *B, int64_t b_rs, int64_t b_cs,
+                             float *C, int64_t c_rs, int64_t c_cs,
+                             int64_t M, int64_t N, int64_t K,
+                             int trans_a, int trans_b, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0) return -1;
+    if (repops_oracle_env_status() != 0) return -2;
+    if (M == 0 || N == 0) return 0;
+    oracle_job base = {A, a_rs, a_cs, B, b_rs, b_cs, C, c_rs, c_cs, M, N, K,
+                       trans_a, trans_b, NULL, NULL, NULL, 0, 0};
+    return run_split(base, M, nthreads);
+}
+
+/*
+ * Selected entries: out[e] = C(ii[e], jj[e]) for 0 <= e < count, for checks
+ * at sizes where the full product is too slow on the CPU.
+ */
+int repops_oracle_entries_f32(const float *A, int64_t a_rs, int64_t a_cs,
+                              const float *B, int64_t b_rs, int64_t b_cs,
+                              int64_t M, int64_t N, int64_t K,
+                              int trans_a, int trans_b,
+                              const int64_t *ii, const int64_t *jj, int64_t count,
+                              float *out, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || count < 0) return -1;
+    if (repops_oracle_env_status() != 0) return -2;
+    for (int64_t e = 0; e < count; ++e)
+        if (ii[e] < 0 || ii[e] >= M || jj[e] < 0 || jj[e] >= N) return -1;
+    if (count == 0) return 0;
+    oracle_job base = {A, a_rs, a_cs, B, b_rs, b_cs, NULL, 0, 0, M, N, K,
+                       trans_a, trans_b, ii, jj, out, 0, 0};
+    return run_split(base, count, nthreads);
+}
