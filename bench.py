@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the reproducible fixed-order FP32 matmul on one MI355X.
+
+One step = one call of the C ABI entry point (host dispatch, operand staging,
+fixed-order accumulation, epilogue) on the Llama-3.1-8B-shaped MLP
+up-projection, M=4096 tokens, K=4096, N=14336, with synthetic operands
+(X ~ N(0,1), W ~ N(0,0.02)) already resident in HBM.  Prints ONE JSON line on
+stdout; progress goes to stderr.
+
+* ``value``: TFLOP/s = 2*M*N*K / (timed wall time / steps).
+* ``roofline``: the dominant (only) kernel's TFLOP/s from HIP events recorded
+  on the launch stream around every timed launch, against the unfused FP32
+  roofline of 78.6 TFLOP/s (256 CUs x 2.4 GHz x 128 flop/clk: one binary32
+  multiply and one binary32 add per multiply-accumulate, two lanes per
+  instruction at the packed rate).  ``traffic`` comes from the committed
+  rocprofv3 FETCH_SIZE/WRITE_SIZE summary when it was taken on the current
+  kernel source, else null.
+* ``cpu_baseline``: the CPU oracle (plain triple loop) timed on a bounded
+  sample of the same workload -- the first R rows of C, all N columns, full
+  K -- on this host's cores.
+* The output is checked bit for bit against the oracle on sampled entries
+  before any number is reported; a mismatch aborts the run.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fixed-order FP32 GEMM TFLOP/s + % of unfused-FP32 VALU peak, bit-exact"
+UNFUSED_PEAK_TFLOPS = 78.6   # 256 CU * 2.4 GHz * 128 flop/clk (packed mul + packed add)
+NONPACKED_PEAK_TFLOPS = 39.3  # the same with one lane op per instruction
+KERNEL_SRC = os.path.join(ROOT, "bit_reproducible_fp32_amd", "csrc", "repops_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "llama8b_mlp_up_traffic.txt")
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+
+
+def committed_traffic(variant_name):
+    """Bytes per launch from the committed counter summary, or None when the
+    summary is missing, was taken for another variant, or predates the
+    current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    fields = dict(re.findall(r"^([a-z_0-9]+):\s*(\S+)\s*$", text, re.M))
+    if fields.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    if fields.get("variant") != variant_name:
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline(A, B, w, target_s):
+    """Oracle throughput on the first R rows of the product (R chosen so the
+    timed run takes about target_s seconds)."""
+    import oracle
+    T = cpu_threads()
+    pilot_rows = max(T, 16)
+    t0 = time.perf_counter()
+    oracle.matmul_f32(A[:pilot_rows], B, w.trans_a, w.trans_b, nthreads=T)
+    pilot = time.perf_counter() - t0
+    rows = int(min(w.M, max(T, pilot_rows * target_s / max(pilot, 1e-3))))
+    rows = max(T, (rows // T) * T)
+    log("cpu baseline: pilot %d rows %.2fs; timing %d rows on %d threads" % (pilot_rows, pilot,
+                                                                             rows, T))
+    t0 = time.perf_counter()
+    oracle.matmul_f32(A[:rows], B, w.trans_a, w.trans_b, nthreads=T)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": T, "kind": "oracle",
+            "sample": "rows 0..%d of C (all %d columns, K=%d): %.3g flop in %.1f s"
+                      % (rows - 1, w.N, w.K, flops, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b_mlp_up")
+    ap.add_argument("--variant", default=None, help="force a kernel variant (name or index)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-torch-sgemm", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the fixed-order matmul shards over output "
+              "tiles with no exchange, and this build runs and reports a single GPU. "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_reproducible_fp32_amd as rp
+    from bit_reproducible_fp32_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    rp.load()  # raises if the HIP library is not built
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS[args.workload]
+    log("workload %s: %s" % (w.name, w.description))
+    A, B = inputs.make_operands(w.name)
+    ga = torch.from_numpy(A).to(dev)
+    gb = torch.from_numpy(B).to(dev)
+    out = torch.empty((w.M, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    if args.variant is None:
+        vidx = rp.repops_pick_variant_f32(ga.data_ptr(), ga.stride(0), ga.stride(1),
+                                          gb.data_ptr(), gb.stride(0), gb.stride(1),
+                                          w.M, w.N, w.K, w.trans_a, w.trans_b)
+    elif args.variant.isdigit():
+        vidx = int(args.variant)
+    else:
+        vidx = rp.variant_names().index(args.variant)
+    vname = rp.repops_variant_name(vidx)
+    log("variant %s" % vname)
+
+    def step():
+        rp.matmul(ga, gb, trans_a=w.trans_a, trans_b=w.trans_b, out=out, variant=vidx,
+                  stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Bit-exactness gate on sampled outputs (the oracle decides).
+    import oracle
+    ii, jj = inputs.sample_entries(w.M, w.N, 512, 2718)
+    want = oracle.entries_f32(A, B, ii, jj, w.trans_a, w.trans_b, nthreads=cpu_threads())
+    got = out.cpu().numpy()[ii, jj]
+    bitexact = bool(np.array_equal(got.view(np.uint32), want.view(np.uint32)))
+    if not bitexact:
+        print("bench.py: output differs from the oracle on sampled entries; no number "
+              "is reported", file=sys.stderr)
+        sys.exit(3)
+    log("bit-exact on %d sampled outputs" % ii.size)
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        starts[s].record(stream)
+        step()
+        ends[s].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [starts[s].elapsed_time(ends[s]) for s in range(args.steps)]
+    ms_per_step = wall * 1e3 / args.steps
+    flops = float(w.flops)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    k_avg_ms = float(np.mean(kernel_ms))
+    achieved = flops / (k_avg_ms * 1e-3) / 1e12
+    log("wall %.3f ms/step, kernel avg %.3f ms (min %.3f, max %.3f): %.2f TFLOP/s"
+        % (ms_per_step, k_avg_ms, min(kernel_ms), max(kernel_ms), achieved))
+    h = hashlib.sha256(out.cpu().numpy().tobytes()).hexdigest()
+
+    extra = {}
+    if not args.no_torch_sgemm:
+        torch.backends.cuda.matmul.allow_tf32 = False
+        opA = ga.t() if w.trans_a else ga
+        opB = gb.t() if w.trans_b else gb
+        ref = torch.empty_like(out)
+        for _ in range(3):
+            torch.matmul(opA, opB, out=ref)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            torch.matmul(opA, opB, out=ref)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_ref = e0.elapsed_time(e1) / args.steps
+        extra["stock_sgemm"] = {
+            "what": "torch.matmul float32 (ROCm BLAS, TF32 off) on the same operands",
+            "ms": round(t_ref, 4), "tflops": round(flops / (t_ref * 1e-3) / 1e12, 3),
+            "overhead": round(k_avg_ms / t_ref - 1.0, 4),
+            "bit_equal_to_oracle_sample": bool(np.array_equal(
+                ref.cpu().numpy()[ii, jj].view(np.uint32), want.view(np.uint32))),
+        }
+        log("stock sgemm %.3f ms -> overhead %.1f%%" % (t_ref, 100 * (k_avg_ms / t_ref - 1)))
+        del ref
+
+    if args.calibrate_copy:
+        n = 256 * 1024 * 1024  # floats: 1 GiB
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 copies of %d bytes" % (4 * n))
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(A, B, w, args.cpu_seconds)
+        log("cpu baseline %.4g TFLOP/s on %d threads" % (cpu["value"], cpu["cores"]))
+
+    traffic = committed_traffic(vname)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "strong",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded numpy PCG64; X ~ N(0,1), W ~ N(0,0.02))",
+        "config": {"workload": "%s M=%d N=%d K=%d" % (w.name, w.M, w.N, w.K),
+                   "M": w.M, "N": w.N, "K": w.K, "trans_a": w.trans_a, "trans_b": w.trans_b,
+                   "variant": vname},
+        "roofline": {"bound": "alu", "achieved": round(achieved, 4),
+                     "peak": UNFUSED_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / UNFUSED_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "frac_of_nonpacked_peak": round(achieved / NONPACKED_PEAK_TFLOPS, 4)},
+        "cpu_baseline": cpu,
+        "bitexact_sampled": bitexact,
+        "sha256_C": h,
+        "kernel_ms": {"mean": round(k_avg_ms, 4), "min": round(min(kernel_ms), 4),
+                      "max": round(max(kernel_ms), 4)},
+    }
+    rec.update(extra)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,92 @@
-"""Reproducible fixed-order FP32 matmul for MI355X (gfx950)."""
+"""Reproducible fixed-order FP32 matrix multiply for AMD MI355X (gfx950).
+
+``matmul(a, b)`` computes C = op(a) op(b) where every output element is
+s = +0; for k ascending: s = RN(s + RN(a_ik * b_kj)) -- the matrix
+multiplication of the RepOps operator library (Verde and RepOps article,
+section 3.2, item 2), with the multiply and the add rounded separately.  The
+bits of C do not depend on the kernel variant, launch shape, transposes or
+strides.
+
+The arithmetic runs in the HIP kernels of ``librepops.so`` behind the C ABI
+declared in ``include/repops.h``; this package only marshals arguments (torch
+supplies device memory and the stream).  Without the built library every
+call raises -- there is no CPU path.
+"""
+from __future__ import annotations
+
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    REPOPS_ERR_ALIAS,
+    REPOPS_ERR_DIM,
+    REPOPS_ERR_HIP,
+    REPOPS_ERR_NULL,
+    REPOPS_ERR_STRIDE,
+    REPOPS_ERR_VARIANT,
+    REPOPS_OK,
+    RepopsError,
+    load,
+    repops_build_manifest,
+    repops_check_args_f32,
+    repops_matmul_f32,
+    repops_matmul_f32_ex,
+    repops_pick_variant_f32,
+    repops_strerror,
+    repops_variant_count,
+    repops_variant_name,
+    variant_names,
+)
+
+
+def _logical(a, b, trans_a, trans_b):
+    M, K = (a.shape[1], a.shape[0]) if trans_a else (a.shape[0], a.shape[1])
+    K2, N = (b.shape[1], b.shape[0]) if trans_b else (b.shape[0], b.shape[1])
+    if K != K2:
+        raise ValueError("inner dimensions differ: op(a) is %dx%d, op(b) is %dx%d" % (M, K, K2, N))
+    return M, N, K
+
+
+def matmul(a, b, *, trans_a: bool = False, trans_b: bool = False, out=None, variant=None,
+           stream=None):
+    """C = op(a) @ op(b) on the GPU, bit-reproducible.
+
+    ``a`` and ``b`` are the stored 2-D float32 CUDA tensors (any strides);
+    ``trans_a``/``trans_b`` select op(x) = x^T.  ``out`` (M x N float32 on the
+    same device, any non-overlapping strides) is overwritten; ``variant``
+    forces a kernel variant (index or name); ``stream`` is a torch stream
+    (default: the current stream).  Returns ``out``.
+    """
+    import torch
+
+    for name, t in (("a", a), ("b", b)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2:
+            raise TypeError("%s must be a 2-D torch tensor" % name)
+        if t.dtype != torch.float32:
+            raise TypeError("%s must be float32" % name)
+        if not t.is_cuda:
+            raise ValueError("%s must be on a GPU; this library has no CPU path" % name)
+    if a.device != b.device:
+        raise ValueError("a and b are on different devices")
+    M, N, K = _logical(a, b, trans_a, trans_b)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    elif out.shape != (M, N) or out.dtype != torch.float32 or out.device != a.device:
+        raise ValueError("out must be float32 of shape (%d, %d) on %s" % (M, N, a.device))
+    if variant is None:
+        v = -1
+    elif isinstance(variant, str):
+        names = variant_names()
+        if variant not in names:
+            raise ValueError("unknown variant %r; known: %s" % (variant, ", ".join(names)))
+        v = names.index(variant)
+    else:
+        v = int(variant)
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device)
+    with torch.cuda.device(a.device):
+        st = repops_matmul_f32_ex(a.data_ptr(), a.stride(0), a.stride(1),
+                                  b.data_ptr(), b.stride(0), b.stride(1),
+                                  out.data_ptr(), out.stride(0), out.stride(1),
+                                  M, N, K, trans_a, trans_b, stream.cuda_stream, v)
+    if st != REPOPS_OK:
+        raise RepopsError(st, "repops_matmul_f32")
+    return out

@@ -1,0 +1,119 @@
+"""ctypes binding of librepops.so: argument marshalling only.
+
+Every entry point of ``include/repops.h`` is exposed under the same name;
+all computation happens in the library's gfx950 kernels.  If the library has
+not been built, loading raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librepops.so")
+
+REPOPS_OK = 0
+REPOPS_ERR_NULL = 1
+REPOPS_ERR_DIM = 2
+REPOPS_ERR_STRIDE = 3
+REPOPS_ERR_ALIAS = 4
+REPOPS_ERR_VARIANT = 5
+REPOPS_ERR_HIP = 6
+
+EXPORTS = (
+    "repops_matmul_f32",
+    "repops_matmul_f32_ex",
+    "repops_check_args_f32",
+    "repops_pick_variant_f32",
+    "repops_variant_count",
+    "repops_variant_name",
+    "repops_strerror",
+    "repops_build_manifest",
+)
+
+_lib = None
+
+
+class RepopsError(RuntimeError):
+    def __init__(self, status: int, where: str = ""):
+        self.status = status
+        msg = "%s: %s (status %d)" % (where or "repops", strerror(status), status)
+        super().__init__(msg)
+
+
+def load():
+    """The loaded library (raises OSError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise OSError("librepops.so is not built (expected at %s); run "
+                      "bit_reproducible_fp32_amd.build.build()" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, ci, cp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_char_p
+    mm = [vp, i64, i64, vp, i64, i64, vp, i64, i64, i64, i64, i64, ci, ci]
+    lib.repops_matmul_f32.argtypes = mm + [vp]
+    lib.repops_matmul_f32.restype = ci
+    lib.repops_matmul_f32_ex.argtypes = mm + [vp, ci]
+    lib.repops_matmul_f32_ex.restype = ci
+    lib.repops_check_args_f32.argtypes = mm + [ci]
+    lib.repops_check_args_f32.restype = ci
+    lib.repops_pick_variant_f32.argtypes = [vp, i64, i64, vp, i64, i64, i64, i64, i64, ci, ci]
+    lib.repops_pick_variant_f32.restype = ci
+    lib.repops_variant_count.argtypes = []
+    lib.repops_variant_count.restype = ci
+    lib.repops_variant_name.argtypes = [ci]
+    lib.repops_variant_name.restype = cp
+    lib.repops_strerror.argtypes = [ci]
+    lib.repops_strerror.restype = cp
+    lib.repops_build_manifest.argtypes = []
+    lib.repops_build_manifest.restype = cp
+    _lib = lib
+    return lib
+
+
+# ---- the C ABI, name for name (pointers and streams are Python ints) -------
+def repops_matmul_f32(A, a_rs, a_cs, B, b_rs, b_cs, C, c_rs, c_cs, M, N, K, trans_a, trans_b,
+                      stream) -> int:
+    return load().repops_matmul_f32(A, a_rs, a_cs, B, b_rs, b_cs, C, c_rs, c_cs, M, N, K,
+                                    int(trans_a), int(trans_b), stream)
+
+
+def repops_matmul_f32_ex(A, a_rs, a_cs, B, b_rs, b_cs, C, c_rs, c_cs, M, N, K, trans_a, trans_b,
+                         stream, variant) -> int:
+    return load().repops_matmul_f32_ex(A, a_rs, a_cs, B, b_rs, b_cs, C, c_rs, c_cs, M, N, K,
+                                       int(trans_a), int(trans_b), stream, int(variant))
+
+
+def repops_check_args_f32(A, a_rs, a_cs, B, b_rs, b_cs, C, c_rs, c_cs, M, N, K, trans_a, trans_b,
+                          variant=-1) -> int:
+    return load().repops_check_args_f32(A, a_rs, a_cs, B, b_rs, b_cs, C, c_rs, c_cs, M, N, K,
+                                        int(trans_a), int(trans_b), int(variant))
+
+
+def repops_pick_variant_f32(A, a_rs, a_cs, B, b_rs, b_cs, M, N, K, trans_a, trans_b) -> int:
+    return load().repops_pick_variant_f32(A, a_rs, a_cs, B, b_rs, b_cs, M, N, K, int(trans_a),
+                                          int(trans_b))
+
+
+def repops_variant_count() -> int:
+    return load().repops_variant_count()
+
+
+def repops_variant_name(variant: int) -> str:
+    return load().repops_variant_name(int(variant)).decode()
+
+
+def repops_strerror(status: int) -> str:
+    return load().repops_strerror(int(status)).decode()
+
+
+def repops_build_manifest() -> str:
+    return load().repops_build_manifest().decode()
+
+
+strerror = repops_strerror
+
+
+def variant_names():
+    return [repops_variant_name(v) for v in range(repops_variant_count())]

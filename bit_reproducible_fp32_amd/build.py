@@ -1,0 +1,59 @@
+"""Builds librepops.so (gfx950) in-tree with hipcc, plus the device assembly
+that the instruction scan in the tests reads.
+
+Flags that matter for the arithmetic:
+
+* ``-ffp-contract=off``: no multiply-add contraction anywhere (the kernels
+  also carry ``#pragma clang fp contract(off)``);
+* ``-fno-fast-math`` and ``-fno-gpu-flush-denormals-to-zero``: IEEE binary32
+  with gradual underflow (kernel descriptors must say denorm mode 3);
+* ``-Xclang -target-feature -Xclang -packed-fp32-ops``: the compiler must not
+  form packed two-lane FP32 instructions.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "librepops.so")
+ASM = os.path.join(HERE, "librepops_gfx950.s")
+ARCH = "gfx950"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+SOURCES = [os.path.join(CSRC, "repops_kernels.hip"), os.path.join(CSRC, "repops_api.cpp")]
+
+FP_FLAGS = ["-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-I", os.path.join(ROOT, "include"),
+          "-Wall", "-Wno-unused-command-line-argument"]
+
+
+def _manifest_defines():
+    flags = " ".join(FP_FLAGS + ["-packed-fp32-ops", "-O3"])
+    return ["-DREPOPS_BUILD_FLAGS=\"%s\"" % flags, "-DREPOPS_OFFLOAD_ARCH=\"%s\"" % ARCH]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into librepops.so and write the gfx950 assembly."""
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *COMMON, *FP_FLAGS, *DEVICE_FLAGS, *_manifest_defines(), "-shared",
+           "-o", tmp, *SOURCES]
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    # Device-only assembly of the kernels, for the instruction scan.
+    asm_tmp = ASM + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *COMMON, *FP_FLAGS, *DEVICE_FLAGS, "--cuda-device-only", "-S",
+           "-o", asm_tmp, SOURCES[0]]
+    subprocess.run(cmd, check=True)
+    os.replace(asm_tmp, ASM)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

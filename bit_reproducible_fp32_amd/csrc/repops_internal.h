@@ -1,0 +1,59 @@
+// Internal interface between the C-ABI front end (repops_api.cpp) and the
+// gfx950 kernels (repops_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <stdint.h>
+
+namespace repops {
+
+// One operand seen as an X x K matrix: element (x, k) is p[x*s_x + k*s_k].
+// For A, x is the output row i; for B, x is the output column j.  Both
+// operands therefore share one loader and one LDS layout.
+struct OperandView {
+    const float* p;
+    int64_t s_x;
+    int64_t s_k;
+    int64_t X;
+};
+
+// Output: element (i, j) is p[i*s_i + j*s_j].
+struct OutView {
+    float* p;
+    int64_t s_i;
+    int64_t s_j;
+};
+
+// How an operand tile is fetched from global memory.
+enum Layout : int {
+    LAY_KC = 0,   // s_k == 1, 16-byte aligned rows: float4 loads along k
+    LAY_XC = 1,   // s_x == 1, 16-byte aligned columns: float4 loads along x
+    LAY_GEN = 2,  // anything else: one element per load
+    LAY_COUNT = 3
+};
+
+// Tile shapes of the register-blocked VALU kernel.
+enum TileCfg : int {
+    CFG_128x128 = 0,  // BM=128 BN=128 BK=16, 8x8 outputs per lane
+    CFG_64x64 = 1,    // BM=64  BN=64  BK=16, 4x4 outputs per lane
+    CFG_128x64 = 2,   // BM=128 BN=64  BK=16, 8x4 outputs per lane
+    CFG_64x128 = 3,   // BM=64  BN=128 BK=16, 4x8 outputs per lane
+    CFG_COUNT = 4
+};
+
+// Workgroup -> output-tile traversal orders (never change a bit).
+enum TileOrder : int {
+    ORDER_ROW = 0,       // tile rows outer, tile columns inner
+    ORDER_COL = 1,       // tile columns outer, tile rows inner
+    ORDER_XCD_GROUP = 2  // contiguous tile ranges per XCD, grouped by 8 tile rows
+};
+
+void tile_shape(int cfg, int* bm, int* bn);
+
+// Each returns a hipError_t value (0 on success) from the launch.
+int launch_tiled(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, OutView C,
+                 int64_t M, int64_t N, int64_t K, int order, void* stream);
+int launch_naive(OperandView A, OperandView B, OutView C, int64_t M, int64_t N, int64_t K,
+                 void* stream);
+int launch_fill_zero(OutView C, int64_t M, int64_t N, void* stream);
+
+}  // namespace repops

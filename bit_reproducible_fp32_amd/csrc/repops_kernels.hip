@@ -1,0 +1,419 @@
+// gfx950 kernels for the reproducible fixed-order FP32 matmul.
+//
+// Every output element is computed by exactly one lane as
+//     s = +0.0f;  for k = 0 .. K-1:  s = RN(s + RN(a_k * b_k));  C(i,j) = s
+// (Verde and RepOps article, section 3.2 "RepOps design principles", item 2:
+// (i, j) may run in any order, k runs in a fixed order).  The multiply and
+// the add are two separately rounded binary32 operations: this file is
+// compiled with -ffp-contract=off and the pragma below, so no fused
+// multiply-add can be formed, and the build's instruction scan rejects any
+// v_fma/v_fmac/v_mad/v_mac/v_dot/packed-FP32 instruction in the result.
+// There is no split-K and no cross-lane reduction: the only thing the tiling
+// changes is which lane computes which (i, j) and when its operands arrive.
+//
+// K tails are padded with +0 on both operands.  A padded step computes
+// s + RN(0 * 0) = s + (+0), which equals s because s is never -0 (it starts
+// at +0, and under round-to-nearest an addition returns -0 only when both
+// addends are -0).  So padding does not change a bit.
+#include <hip/hip_runtime.h>
+
+#include "repops_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace repops {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPad = 4;  // LDS row padding (floats); keeps rows 16-byte aligned
+
+// Binary32 multiply and add, each rounded on its own (contraction is off).
+__device__ __forceinline__ float mul_rn(float a, float b) { return a * b; }
+__device__ __forceinline__ float add_rn(float a, float b) { return a + b; }
+
+// ---------------------------------------------------------------------------
+// Global -> register -> LDS staging of one X x BK operand tile.
+// LDS holds the tile k-major: lds[k * (BX + kPad) + x].  Each lane owns kNV
+// loads at fixed tile coordinates; their addresses are formed once and
+// advanced by BK * s_k per k-tile.
+//
+// Rows beyond the operand (x >= X) are clamped to a valid row: they only feed
+// outputs that are never stored, so their values do not matter and the
+// steady-state loads need no masks.  Only the last, partial k-tile (when BK
+// does not divide K) is masked, and there both operands read +0 for k >= K.
+template <int BX, int BK, int LAY>
+struct TileStage {
+    static constexpr int kElems = BX * BK / kThreads;  // floats per lane
+    static constexpr int kVec = (LAY == LAY_GEN) ? 1 : 4;
+    static constexpr int kNV = kElems / kVec;          // loads per lane
+    static constexpr int kLd = BX + kPad;
+    static_assert(kElems * kThreads == BX * BK, "tile must split evenly over lanes");
+    static_assert(kNV * kVec == kElems, "vector loads must split evenly");
+
+    float r[kElems];
+    const float* src[kNV];  // address of load v in the next k-tile to load
+    int kofs[kNV];          // k offset of load v inside its tile
+    int64_t step;           // BK * s_k
+
+    // Coordinates (x, k) inside the tile of the first element of load v.
+    __device__ static void coords(int tid, int v, int& x, int& k) {
+        const int f = tid + kThreads * v;
+        if constexpr (LAY == LAY_KC) {         // 4 consecutive k of one row
+            x = f / (BK / 4);
+            k = (f % (BK / 4)) * 4;
+        } else if constexpr (LAY == LAY_XC) {  // 4 consecutive x of one k
+            x = (f % (BX / 4)) * 4;
+            k = f / (BX / 4);
+        } else {                               // consecutive lanes, consecutive x
+            x = f % BX;
+            k = f / BX;
+        }
+    }
+
+    __device__ void init(const OperandView& op, int64_t x0, int tid) {
+        step = static_cast<int64_t>(BK) * op.s_k;
+#pragma unroll
+        for (int v = 0; v < kNV; ++v) {
+            int x, k;
+            coords(tid, v, x, k);
+            int64_t gx = x0 + x;
+            // LAY_XC is only chosen when 4 divides X, so a clamped vector
+            // start X-4 keeps all four elements inside the operand.
+            const int64_t last = (LAY == LAY_XC) ? op.X - 4 : op.X - 1;
+            gx = gx < last ? gx : last;
+            kofs[v] = k;
+            src[v] = op.p + gx * op.s_x + static_cast<int64_t>(k) * op.s_k;
+        }
+    }
+
+    // A k-tile that lies entirely inside [0, K).
+    __device__ void load_full() {
+#pragma unroll
+        for (int v = 0; v < kNV; ++v) {
+            const float* p = src[v];
+            src[v] = p + step;
+            if constexpr (LAY == LAY_GEN) {
+                r[v] = *p;
+            } else {
+                const float4 q = *reinterpret_cast<const float4*>(p);
+                r[4 * v + 0] = q.x; r[4 * v + 1] = q.y; r[4 * v + 2] = q.z; r[4 * v + 3] = q.w;
+            }
+        }
+    }
+
+    // The k-tile starting at k0 that crosses K: elements with k >= K read +0.
+    __device__ void load_tail(int64_t k0, int64_t K, int64_t s_k) {
+#pragma unroll
+        for (int v = 0; v < kNV; ++v) {
+            const float* p = src[v];
+            src[v] = p + step;
+            const int64_t gk = k0 + kofs[v];
+            if constexpr (LAY == LAY_GEN) {
+                r[v] = gk < K ? *p : 0.0f;
+            } else if constexpr (LAY == LAY_KC) {  // s_k == 1: 4 consecutive k
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r[4 * v + e] = gk + e < K ? p[e] : 0.0f;
+            } else {                               // one k, 4 consecutive x
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r[4 * v + e] = gk < K ? p[e] : 0.0f;
+            }
+        }
+        (void)s_k;
+    }
+
+    __device__ void store(float* lds, int tid) const {
+#pragma unroll
+        for (int v = 0; v < kNV; ++v) {
+            int x, k;
+            coords(tid, v, x, k);
+            if constexpr (LAY == LAY_GEN) {
+                lds[k * kLd + x] = r[v];
+            } else if constexpr (LAY == LAY_KC) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) lds[(k + e) * kLd + x] = r[4 * v + e];
+            } else {
+                *reinterpret_cast<float4*>(&lds[k * kLd + x]) =
+                    make_float4(r[4 * v + 0], r[4 * v + 1], r[4 * v + 2], r[4 * v + 3]);
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Workgroup -> (tile row, tile column).  Any bijection is correct; these
+// orders only change cache reuse.
+__device__ __forceinline__ void tile_of_block(int order, int tiles_m, int tiles_n, int& tm,
+                                              int& tn) {
+    int w = static_cast<int>(blockIdx.x);
+    if (order == ORDER_ROW) {
+        tm = w / tiles_n;
+        tn = w % tiles_n;
+        return;
+    }
+    if (order == ORDER_COL) {
+        tn = w / tiles_m;
+        tm = w % tiles_m;
+        return;
+    }
+    // Workgroups are dealt round-robin to the 8 XCDs, each with its own L2.
+    // Give XCD x the contiguous tile range [x*per, (x+1)*per) so tiles that
+    // share operand panels meet in one L2; the remainder keeps its identity.
+    const int total = tiles_m * tiles_n;
+    const int per = total / 8;
+    int t = w;
+    if (w < per * 8) t = (w % 8) * per + (w / 8);
+    // Then walk groups of 8 tile rows, tile rows fastest inside a group.
+    constexpr int kGroup = 8;
+    const int span = kGroup * tiles_n;
+    const int first_m = (t / span) * kGroup;
+    const int rows = min(tiles_m - first_m, kGroup);
+    const int local = t % span;
+    tm = first_m + local % rows;
+    tn = local / rows;
+}
+
+// The TM row operands and TN column operands of one k step, as float4 reads
+// of the k-major LDS tiles (as/bs already offset by the lane's ty*4 / tx*4).
+template <int RG, int CG, int RSPAN, int CSPAN>
+__device__ __forceinline__ void read_lane_operands(const float* as, const float* bs, float* a,
+                                                   float* b) {
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+        const float4 q = *reinterpret_cast<const float4*>(as + g * RSPAN);
+        a[4 * g + 0] = q.x; a[4 * g + 1] = q.y; a[4 * g + 2] = q.z; a[4 * g + 3] = q.w;
+    }
+#pragma unroll
+    for (int h = 0; h < CG; ++h) {
+        const float4 q = *reinterpret_cast<const float4*>(bs + h * CSPAN);
+        b[4 * h + 0] = q.x; b[4 * h + 1] = q.y; b[4 * h + 2] = q.z; b[4 * h + 3] = q.w;
+    }
+}
+
+// BK ascending k steps of one lane's TM x TN block: acc += a*b, the multiply
+// and the add separately rounded.  Operands of step k+1 are read into the
+// other register set while step k computes, so only two steps of operands
+// are ever live.
+template <int BK, int TM, int TN, int RSPAN, int CSPAN, int LDA, int LDB>
+__device__ __forceinline__ void lane_tile_steps(const float* as, const float* bs,
+                                                float (&acc)[TM][TN]) {
+    constexpr int RG = TM / 4, CG = TN / 4;
+    float a[2][TM], b[2][TN];
+    read_lane_operands<RG, CG, RSPAN, CSPAN>(as, bs, a[0], b[0]);
+#pragma unroll
+    for (int k = 0; k < BK; ++k) {
+        const int c = k & 1;
+        if (k + 1 < BK)
+            read_lane_operands<RG, CG, RSPAN, CSPAN>(as + (k + 1) * LDA, bs + (k + 1) * LDB,
+                                                     a[c ^ 1], b[c ^ 1]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = add_rn(acc[i][j], mul_rn(a[c][i], b[c][j]));
+        // Pin step k's adds here: an empty volatile asm that reads and writes
+        // each accumulator is ordered with the LDS reads, so the instruction
+        // selector cannot sink the arithmetic below later reads.
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(acc[i][j]));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Register-blocked VALU kernel.  256 lanes own a BM x BN output tile; lane
+// (ty, tx) owns TM x TN outputs in groups of 4 consecutive rows/columns:
+// rows g*(BM/(TM/4)) + ty*4 + e, columns h*(BN/(TN/4)) + tx*4 + f.  Operand
+// tiles are double-buffered in LDS with one barrier per BK step.
+template <int BM, int BN, int BK, int TM, int TN, int LA, int LB>
+__global__ __launch_bounds__(kThreads) void repops_tiled_kernel(OperandView A, OperandView B,
+                                                                OutView C, int64_t M, int64_t N,
+                                                                int64_t K, int tiles_m,
+                                                                int tiles_n, int order) {
+    static_assert((BM / TM) * (BN / TN) == kThreads, "one lane per TM x TN block");
+    static_assert(TM % 4 == 0 && TN % 4 == 0, "lane blocks are groups of 4");
+    constexpr int RG = TM / 4, CG = TN / 4;
+    constexpr int RSPAN = BM / RG, CSPAN = BN / CG;
+    constexpr int LDA = BM + kPad, LDB = BN + kPad;
+
+    __shared__ __attribute__((aligned(16))) float As[2][BK * LDA];
+    __shared__ __attribute__((aligned(16))) float Bs[2][BK * LDB];
+
+    const int tid = static_cast<int>(threadIdx.x);
+    const int tx = tid % (BN / TN);
+    const int ty = tid / (BN / TN);
+    int tm, tn;
+    tile_of_block(order, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = static_cast<int64_t>(tm) * BM;
+    const int64_t n0 = static_cast<int64_t>(tn) * BN;
+
+    float acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = 0.0f;  // s = +0
+
+    TileStage<BM, BK, LA> sa;
+    TileStage<BN, BK, LB> sb;
+    sa.init(A, m0, tid);
+    sb.init(B, n0, tid);
+    const int64_t nfull = K / BK;              // k-tiles entirely inside [0, K)
+    const bool tail = (K % BK) != 0;           // one more, partial k-tile
+    const float* as0 = &As[0][ty * 4];
+    const float* bs0 = &Bs[0][tx * 4];
+    const float* as1 = &As[1][ty * 4];
+    const float* bs1 = &Bs[1][tx * 4];
+
+    if (nfull > 0) {
+        sa.load_full();
+        sb.load_full();
+    } else {
+        sa.load_tail(0, K, A.s_k);
+        sb.load_tail(0, K, B.s_k);
+    }
+    sa.store(As[0], tid);
+    sb.store(Bs[0], tid);
+    __syncthreads();
+
+    // k-tile kt sits in LDS buffer kt&1 while tile kt+1 is fetched into
+    // registers.  One copy of the compute: the next-tile loads sit behind
+    // uniform branches, fenced off by empty asm memory barriers so the
+    // compiler cannot move the compute's LDS reads across them.
+    const int64_t ktiles = nfull + (tail ? 1 : 0);
+    for (int64_t kt = 0; kt < ktiles; ++kt) {
+        const bool more = kt + 1 < ktiles;
+        if (kt + 1 < nfull) {
+            sa.load_full();
+            sb.load_full();
+        } else if (more) {
+            sa.load_tail(nfull * BK, K, A.s_k);
+            sb.load_tail(nfull * BK, K, B.s_k);
+        }
+        asm volatile("" ::: "memory");
+        const bool odd = (kt & 1) != 0;
+        lane_tile_steps<BK, TM, TN, RSPAN, CSPAN, LDA, LDB>(odd ? as1 : as0, odd ? bs1 : bs0, acc);
+        asm volatile("" ::: "memory");
+        if (more) {
+            sa.store(odd ? As[0] : As[1], tid);
+            sb.store(odd ? Bs[0] : Bs[1], tid);
+        }
+        __syncthreads();
+    }
+
+    // Epilogue: plain stores of s; C is never read.
+    const bool vec_store = (C.s_j == 1) && ((C.s_i & 3) == 0) &&
+                           ((reinterpret_cast<uintptr_t>(C.p) & 15) == 0);
+#pragma unroll
+    for (int g = 0; g < RG; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t i = m0 + g * RSPAN + ty * 4 + e;
+            if (i >= M) continue;
+#pragma unroll
+            for (int h = 0; h < CG; ++h) {
+                const int64_t j0 = n0 + h * CSPAN + tx * 4;
+                const float* v = &acc[4 * g + e][4 * h];
+                if (vec_store && j0 + 3 < N) {
+                    *reinterpret_cast<float4*>(C.p + i * C.s_i + j0) = make_float4(v[0], v[1], v[2], v[3]);
+                } else {
+#pragma unroll
+                    for (int f = 0; f < 4; ++f)
+                        if (j0 + f < N) C.p[i * C.s_i + (j0 + f) * C.s_j] = v[f];
+                }
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// One lane per output, operands straight from global memory.  The plainest
+// GPU form of the definition; every other variant must match it bit for bit.
+__global__ __launch_bounds__(256) void repops_naive_kernel(OperandView A, OperandView B,
+                                                          OutView C, int64_t M, int64_t N,
+                                                          int64_t K, int blocks_n) {
+    const int bx = static_cast<int>(blockIdx.x) % blocks_n;
+    const int by = static_cast<int>(blockIdx.x) / blocks_n;
+    const int64_t i = static_cast<int64_t>(by) * 16 + threadIdx.x / 16;
+    const int64_t j = static_cast<int64_t>(bx) * 16 + threadIdx.x % 16;
+    if (i >= M || j >= N) return;
+    const float* a = A.p + i * A.s_x;
+    const float* b = B.p + j * B.s_x;
+    float s = 0.0f;
+    for (int64_t k = 0; k < K; ++k) s = add_rn(s, mul_rn(a[k * A.s_k], b[k * B.s_k]));
+    C.p[i * C.s_i + j * C.s_j] = s;
+}
+
+// K == 0: every output is the empty sum, +0.  Grid-stride over rows and
+// columns (no integer division).
+__global__ __launch_bounds__(256) void repops_fill_zero_kernel(OutView C, int64_t M, int64_t N) {
+    for (int64_t i = blockIdx.x; i < M; i += gridDim.x)
+        for (int64_t j = threadIdx.x; j < N; j += 256) C.p[i * C.s_i + j * C.s_j] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+using TiledFn = void (*)(OperandView, OperandView, OutView, int64_t, int64_t, int64_t, int, int,
+                         int);
+
+template <int BM, int BN, int BK, int TM, int TN>
+struct CfgTable {
+    using Fn = TiledFn;
+    template <int LA, int LB>
+    static constexpr Fn fn() { return &repops_tiled_kernel<BM, BN, BK, TM, TN, LA, LB>; }
+    static Fn get(int la, int lb) {
+        static const Fn t[LAY_COUNT][LAY_COUNT] = {
+            {fn<0, 0>(), fn<0, 1>(), fn<0, 2>()},
+            {fn<1, 0>(), fn<1, 1>(), fn<1, 2>()},
+            {fn<2, 0>(), fn<2, 1>(), fn<2, 2>()},
+        };
+        return t[la][lb];
+    }
+};
+
+}  // namespace
+
+void tile_shape(int cfg, int* bm, int* bn) {
+    switch (cfg) {
+        case CFG_128x128: *bm = 128; *bn = 128; break;
+        case CFG_64x64: *bm = 64; *bn = 64; break;
+        case CFG_128x64: *bm = 128; *bn = 64; break;
+        default: *bm = 64; *bn = 128; break;
+    }
+}
+
+int launch_tiled(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, OutView C,
+                 int64_t M, int64_t N, int64_t K, int order, void* stream) {
+    int bm, bn;
+    tile_shape(cfg, &bm, &bn);
+    const int tiles_m = static_cast<int>((M + bm - 1) / bm);
+    const int tiles_n = static_cast<int>((N + bn - 1) / bn);
+    const dim3 grid(static_cast<unsigned>(tiles_m) * static_cast<unsigned>(tiles_n));
+    const dim3 block(kThreads);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    TiledFn fn;
+    switch (cfg) {
+        case CFG_128x128: fn = CfgTable<128, 128, 16, 8, 8>::get(lay_a, lay_b); break;
+        case CFG_64x64: fn = CfgTable<64, 64, 16, 4, 4>::get(lay_a, lay_b); break;
+        case CFG_128x64: fn = CfgTable<128, 64, 16, 8, 4>::get(lay_a, lay_b); break;
+        default: fn = CfgTable<64, 128, 16, 4, 8>::get(lay_a, lay_b); break;
+    }
+    hipLaunchKernelGGL(fn, grid, block, 0, s, A, B, C, M, N, K, tiles_m, tiles_n, order);
+    return static_cast<int>(hipGetLastError());
+}
+
+int launch_naive(OperandView A, OperandView B, OutView C, int64_t M, int64_t N, int64_t K,
+                 void* stream) {
+    const int blocks_n = static_cast<int>((N + 15) / 16);
+    const int blocks_m = static_cast<int>((M + 15) / 16);
+    hipLaunchKernelGGL(repops_naive_kernel,
+                       dim3(static_cast<unsigned>(blocks_m) * static_cast<unsigned>(blocks_n)),
+                       dim3(256), 0, static_cast<hipStream_t>(stream), A, B, C, M, N, K, blocks_n);
+    return static_cast<int>(hipGetLastError());
+}
+
+int launch_fill_zero(OutView C, int64_t M, int64_t N, void* stream) {
+    const unsigned blocks = static_cast<unsigned>(M < 65536 ? M : 65536);
+    hipLaunchKernelGGL(repops_fill_zero_kernel, dim3(blocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), C, M, N);
+    return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace repops

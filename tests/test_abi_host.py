@@ -1,0 +1,215 @@
+"""Host-side checks of the C ABI that need no GPU.
+
+* librepops.so loads and exports every function include/repops.h declares;
+* argument validation (run through repops_check_args_f32 and through
+  repops_matmul_f32 itself: invalid calls return before any device work);
+* variant table, status strings and the build manifest;
+* the instruction scan of the gfx950 assembly built from the same sources:
+  no fused or packed FP32, no dot or matrix instructions in the VALU
+  kernels, IEEE denormals and round-to-nearest-even in every kernel
+  descriptor, no register spills in the tiled kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import bit_reproducible_fp32_amd as rp
+from bit_reproducible_fp32_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "repops.h")
+ASM = os.path.join(ROOT, "bit_reproducible_fp32_amd", "librepops_gfx950.s")
+
+# Fake, never-dereferenced addresses: validation compares them only.
+PA, PB, PC = 0x10000000, 0x20000000, 0x30000000
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(repops_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = _lib.load()
+    declared = header_functions()
+    assert declared, "no declarations parsed"
+    for name in declared:
+        assert hasattr(lib, name), "missing export %s" % name
+    assert sorted(_lib.EXPORTS) == declared
+
+
+def test_binding_has_the_same_names():
+    for name in header_functions():
+        assert callable(getattr(rp, name)), name
+
+
+def ok(**kw):
+    args = dict(A=PA, a_rs=64, a_cs=1, B=PB, b_rs=32, b_cs=1, C=PC, c_rs=32, c_cs=1,
+                M=16, N=32, K=64, trans_a=0, trans_b=0, variant=-1)
+    args.update(kw)
+    return rp.repops_check_args_f32(**args)
+
+
+def test_valid_arguments_pass():
+    assert ok() == rp.REPOPS_OK
+    assert ok(trans_a=1, a_rs=16, a_cs=1) == rp.REPOPS_OK
+    assert ok(trans_b=1, b_rs=64, b_cs=1) == rp.REPOPS_OK
+    assert ok(a_rs=0, a_cs=0) == rp.REPOPS_OK  # broadcast operand
+    assert ok(c_rs=1, c_cs=16) == rp.REPOPS_OK  # column-major output
+    for v in range(rp.repops_variant_count()):
+        assert ok(variant=v) == rp.REPOPS_OK
+
+
+def test_dimension_errors():
+    assert ok(M=-1) == rp.REPOPS_ERR_DIM
+    assert ok(N=-5) == rp.REPOPS_ERR_DIM
+    assert ok(K=-1) == rp.REPOPS_ERR_DIM
+    assert ok(trans_a=2) == rp.REPOPS_ERR_DIM
+    assert ok(trans_b=-1) == rp.REPOPS_ERR_DIM
+    assert ok(a_rs=2 ** 62) == rp.REPOPS_ERR_DIM  # offset overflow
+    assert ok(M=2 ** 40, N=2 ** 40, c_rs=2 ** 40) == rp.REPOPS_ERR_DIM  # grid too large
+
+
+def test_null_errors_and_empty_problems():
+    assert ok(A=0) == rp.REPOPS_ERR_NULL
+    assert ok(B=0) == rp.REPOPS_ERR_NULL
+    assert ok(C=0) == rp.REPOPS_ERR_NULL
+    assert ok(A=0, B=0, K=0) == rp.REPOPS_OK     # K = 0: operands unused
+    assert ok(A=0, B=0, C=0, M=0) == rp.REPOPS_OK  # nothing to do
+    assert ok(A=0, B=0, C=0, N=0) == rp.REPOPS_OK
+
+
+def test_stride_errors():
+    assert ok(a_rs=-64) == rp.REPOPS_ERR_STRIDE
+    assert ok(b_cs=-1) == rp.REPOPS_ERR_STRIDE
+    assert ok(c_rs=0) == rp.REPOPS_ERR_STRIDE    # two rows on one address
+    assert ok(c_cs=0) == rp.REPOPS_ERR_STRIDE
+    assert ok(c_rs=16) == rp.REPOPS_ERR_STRIDE   # rows overlap (N = 32)
+    assert ok(M=1, c_rs=0) == rp.REPOPS_OK       # one row: its stride is unused
+
+
+def test_alias_errors():
+    # C starts inside A's span: A spans 16*64 floats from PA.
+    assert ok(C=PA + 4 * 100) == rp.REPOPS_ERR_ALIAS
+    assert ok(C=PB) == rp.REPOPS_ERR_ALIAS
+    # C ends exactly where A starts: no overlap.
+    assert ok(C=PA - 4 * 16 * 32) == rp.REPOPS_OK
+    assert ok(C=PA - 4 * 16 * 32 + 4) == rp.REPOPS_ERR_ALIAS
+    # K = 0 reads neither operand, so no alias is possible.
+    assert ok(C=PA, K=0) == rp.REPOPS_OK
+
+
+def test_variant_errors_and_table():
+    n = rp.repops_variant_count()
+    assert n >= 5
+    assert ok(variant=n) == rp.REPOPS_ERR_VARIANT
+    assert ok(variant=-2) == rp.REPOPS_ERR_VARIANT
+    names = rp.variant_names()
+    assert len(set(names)) == n and all(names)
+    assert rp.repops_variant_name(n) == "?"
+    assert names[0].startswith("naive")
+
+
+def test_matmul_entry_rejects_before_any_device_work():
+    """Invalid calls return their status from the real entry point (no GPU here)."""
+    st = rp.repops_matmul_f32(PA, 64, 1, PB, 32, 1, PA, 32, 1, 16, 32, 64, 0, 0, 0)
+    assert st == rp.REPOPS_ERR_ALIAS
+    st = rp.repops_matmul_f32_ex(PA, 64, 1, PB, 32, 1, PC, 32, 1, 16, 32, 64, 0, 0, 0, 999)
+    assert st == rp.REPOPS_ERR_VARIANT
+    assert rp.repops_matmul_f32(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 5, 5, 0, 0, 0) == rp.REPOPS_OK
+
+
+def test_pick_variant():
+    big = rp.repops_pick_variant_f32(PA, 4096, 1, PB, 14336, 1, 4096, 14336, 4096, 0, 0)
+    small = rp.repops_pick_variant_f32(PA, 256, 1, PB, 256, 1, 256, 256, 256, 0, 0)
+    assert 0 <= big < rp.repops_variant_count() and 0 <= small < rp.repops_variant_count()
+    assert rp.repops_pick_variant_f32(PA, 1, 1, PB, 1, 1, 0, 1, 1, 0, 0) == -1
+
+
+def test_strerror_and_manifest():
+    for st in range(7):
+        assert rp.repops_strerror(st)
+    assert rp.repops_strerror(99) == "unknown status"
+    man = json.loads(rp.repops_build_manifest())
+    assert man["offload_arch"] == "gfx950"
+    assert "-ffp-contract=off" in man["flags"]
+    assert man["variants"] == rp.variant_names()
+
+
+def test_python_wrapper_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    a = torch.zeros(4, 4)
+    with pytest.raises(ValueError):
+        rp.matmul(a, a)
+
+
+# ---------------------------------------------------------------- instruction scan
+FORBIDDEN_FP = re.compile(
+    r"^\s+(v_fma\w*|v_fmac\w*|v_mad_(f16|f32|legacy\w*|mix\w*)|v_mac_\w*|v_pk_fma_f32|"
+    r"v_pk_mul_f32|v_pk_add_f32|v_dot\w*|v_fma_mix\w*)\b", re.M)
+MATRIX = re.compile(r"^\s+v_(s)?mfma\w*", re.M)
+
+
+def kernels():
+    text = open(ASM).read()
+    out = {}
+    for m in re.finditer(r"^(_Z\w+):[ \t]*(;.*)?$", text, re.M):
+        name = m.group(1)
+        end = text.find(".Lfunc_end", m.end())
+        out[name] = text[m.end():end]
+    descs = dict(re.findall(r"\.amdhsa_kernel (\S+)\n(.*?)\.end_amdhsa_kernel", text, re.S))
+    return out, descs
+
+
+def test_isa_has_no_fused_or_packed_fp32():
+    bodies, _ = kernels()
+    assert bodies
+    for name, body in bodies.items():
+        bad = FORBIDDEN_FP.findall(body)
+        assert not bad, "%s uses %s" % (name, bad[:3])
+
+
+def test_isa_valu_kernels_use_no_matrix_instructions():
+    bodies, _ = kernels()
+    for name, body in bodies.items():
+        if "tiled_kernel" in name or "naive_kernel" in name:
+            assert not MATRIX.search(body), name
+
+
+def test_isa_mul_and_add_present_in_tiled_kernels():
+    bodies, _ = kernels()
+    tiled = [b for n, b in bodies.items() if "tiled_kernel" in n]
+    assert tiled
+    for b in tiled:
+        assert "v_mul_f32" in b and "v_add_f32" in b
+
+
+def test_kernel_descriptors_ieee_denormals_and_rne():
+    _, descs = kernels()
+    assert descs
+    for name, d in descs.items():
+        assert re.search(r"\.amdhsa_float_denorm_mode_32 3\b", d), name
+        assert re.search(r"\.amdhsa_float_round_mode_32 0\b", d), name
+
+
+def test_tiled_kernels_do_not_spill():
+    text = open(ASM).read()
+    for block in text.split("  - .agpr_count:")[1:]:
+        name = re.search(r"\.name:\s+(\S+)", block).group(1)
+        if "tiled_kernel" not in name:
+            continue
+        spill = int(re.search(r"\.vgpr_spill_count:\s+(\d+)", block).group(1))
+        priv = int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", block).group(1))
+        assert spill == 0 and priv == 0, name
+
+
+def test_assembly_matches_the_library_build():
+    """The scanned assembly is at least as new as the kernel source."""
+    src = os.path.join(ROOT, "bit_reproducible_fp32_amd", "csrc", "repops_kernels.hip")
+    assert os.path.getmtime(ASM) >= os.path.getmtime(src) - 1
