@@ -27,7 +27,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = [os.path.join(CSRC, "repops_kernels.hip"), os.path.join(CSRC, "repops_api.cpp")]
 
 FP_FLAGS = ["-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero"]
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # matrix-instruction results land in ordinary VGPRs, where the
+                # VALU adds read them (no accumulation-register copies)
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-I", os.path.join(ROOT, "include"),
           "-Wall", "-Wno-unused-command-line-argument"]
 

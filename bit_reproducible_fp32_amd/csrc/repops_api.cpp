@@ -20,7 +20,7 @@ using namespace repops;
 
 namespace {
 
-enum Kind { KIND_NAIVE = 0, KIND_TILED = 1 };
+enum Kind { KIND_NAIVE = 0, KIND_TILED = 1, KIND_MPROD = 2 };
 
 struct Variant {
     const char* name;
@@ -40,10 +40,23 @@ const Variant kVariants[] = {
     {"valu_t64x64x16_r4x4_xcd", KIND_TILED, CFG_64x64, ORDER_XCD_GROUP},
     {"valu_t128x64x16_r8x4_xcd", KIND_TILED, CFG_128x64, ORDER_XCD_GROUP},
     {"valu_t64x128x16_r4x8_col", KIND_TILED, CFG_64x128, ORDER_COL},
+    {"mprod_t128x128x16_w4_xcd", KIND_MPROD, MCFG_128x128_W4, ORDER_XCD_GROUP},
+    {"mprod_t128x128x16_w8_xcd", KIND_MPROD, MCFG_128x128_W8, ORDER_XCD_GROUP},
+    {"mprod_t256x128x16_w8_xcd", KIND_MPROD, MCFG_256x128_W8, ORDER_XCD_GROUP},
+    {"mprod_t64x64x16_w2_row", KIND_MPROD, MCFG_64x64_W2, ORDER_ROW},
+    {"mprod_t128x128x16_w4_col", KIND_MPROD, MCFG_128x128_W4, ORDER_COL},
+    {"mprod1_t128x128x16_w8_xcd", KIND_MPROD, MCFG_128x128_W8_P1, ORDER_XCD_GROUP},
+    {"mprod1_t128x128x16_w4_xcd", KIND_MPROD, MCFG_128x128_W4_P1, ORDER_XCD_GROUP},
+    {"mprod1_t256x128x16_w8_xcd", KIND_MPROD, MCFG_256x128_W8_P1, ORDER_XCD_GROUP},
 };
 constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVariants[0]));
-constexpr int kVariantAutoLarge = 3;  // valu_t128x128x16_r8x8_xcd
-constexpr int kVariantAutoSmall = 5;  // valu_t64x64x16_r4x4_xcd
+
+// Index of a variant by name (-1 if absent).
+int variant_index(const char* name) {
+    for (int v = 0; v < kNumVariants; ++v)
+        if (strcmp(kVariants[v].name, name) == 0) return v;
+    return -1;
+}
 
 // Work-items in one dispatch must fit the 32-bit grid size.
 constexpr int64_t kMaxBlocks = (int64_t(1) << 32) / 256 - 1;
@@ -163,11 +176,11 @@ int classify(const OperandView& v, int64_t K) {
 }
 
 int pick(const Problem& p) {
-    int bm, bn;
-    tile_shape(CFG_128x128, &bm, &bn);
-    const int64_t tiles = ((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn);
+    static const int large = variant_index("mprod1_t128x128x16_w8_xcd");
+    static const int small = variant_index("mprod_t64x64x16_w2_row");
+    const int64_t tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128);
     // 256 CUs: 128x128 tiles when there are at least two per CU, else 64x64.
-    return tiles >= 512 ? kVariantAutoLarge : kVariantAutoSmall;
+    return tiles >= 512 ? large : small;
 }
 
 repops_status run(const Problem& p, int variant, void* stream) {
@@ -180,6 +193,9 @@ repops_status run(const Problem& p, int variant, void* stream) {
         const Variant& var = kVariants[v];
         if (var.kind == KIND_NAIVE) {
             err = launch_naive(p.a, p.b, p.c, p.M, p.N, p.K, stream);
+        } else if (var.kind == KIND_MPROD) {
+            err = launch_mprod(var.cfg, classify(p.a, p.K), classify(p.b, p.K), p.a, p.b, p.c,
+                               p.M, p.N, p.K, var.order, stream);
         } else {
             err = launch_tiled(var.cfg, classify(p.a, p.K), classify(p.b, p.K), p.a, p.b, p.c,
                                p.M, p.N, p.K, var.order, stream);

@@ -37,7 +37,16 @@ enum TileCfg : int {
     CFG_64x64 = 1,    // BM=64  BN=64  BK=16, 4x4 outputs per lane
     CFG_128x64 = 2,   // BM=128 BN=64  BK=16, 8x4 outputs per lane
     CFG_64x128 = 3,   // BM=64  BN=128 BK=16, 4x8 outputs per lane
-    CFG_COUNT = 4
+    // Matrix-core-product kernels (products on the matrix core, sums on the
+    // VALU): tile, waves per workgroup.
+    MCFG_128x128_W4 = 4,  // 2x2 waves, each 64 rows x 2 blocks of 32 columns
+    MCFG_128x128_W8 = 5,  // 2x4 waves, each 64 rows x 32 columns
+    MCFG_256x128_W8 = 6,  // 4x2 waves, each 64 rows x 2 blocks of 32 columns
+    MCFG_64x64_W2 = 7,    // 1x2 waves, each 64 rows x 32 columns
+    // The same with one product buffer per wave (fewer registers, more waves).
+    MCFG_128x128_W8_P1 = 8,
+    MCFG_128x128_W4_P1 = 9,
+    MCFG_256x128_W8_P1 = 10,
 };
 
 // Workgroup -> output-tile traversal orders (never change a bit).
@@ -47,10 +56,27 @@ enum TileOrder : int {
     ORDER_XCD_GROUP = 2  // contiguous tile ranges per XCD, grouped by 8 tile rows
 };
 
+// Integer division by a runtime divisor as a multiply and shift:
+// floor(n / d) == (n * m) >> s for 0 <= n < 2^31 (see make_fastdiv).
+struct FastDiv {
+    uint32_t d, m, s;
+};
+
+// Tile grid of one launch: tile counts, traversal order and the divisors the
+// workgroup -> tile mapping needs.
+struct TileGrid {
+    int tiles_m, tiles_n, order;
+    FastDiv div_n, div_m, div_span, div_last;
+};
+
+FastDiv make_fastdiv(uint32_t d);
+TileGrid make_tile_grid(int tiles_m, int tiles_n, int order);
 void tile_shape(int cfg, int* bm, int* bn);
 
 // Each returns a hipError_t value (0 on success) from the launch.
 int launch_tiled(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, OutView C,
+                 int64_t M, int64_t N, int64_t K, int order, void* stream);
+int launch_mprod(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, OutView C,
                  int64_t M, int64_t N, int64_t K, int order, void* stream);
 int launch_naive(OperandView A, OperandView B, OutView C, int64_t M, int64_t N, int64_t K,
                  void* stream);

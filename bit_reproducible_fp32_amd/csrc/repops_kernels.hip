@@ -41,13 +41,13 @@ __device__ __forceinline__ float add_rn(float a, float b) { return a + b; }
 // outputs that are never stored, so their values do not matter and the
 // steady-state loads need no masks.  Only the last, partial k-tile (when BK
 // does not divide K) is masked, and there both operands read +0 for k >= K.
-template <int BX, int BK, int LAY>
+template <int BX, int BK, int LAY, int NT = kThreads>
 struct TileStage {
-    static constexpr int kElems = BX * BK / kThreads;  // floats per lane
+    static constexpr int kElems = BX * BK / NT;        // floats per lane
     static constexpr int kVec = (LAY == LAY_GEN) ? 1 : 4;
     static constexpr int kNV = kElems / kVec;          // loads per lane
     static constexpr int kLd = BX + kPad;
-    static_assert(kElems * kThreads == BX * BK, "tile must split evenly over lanes");
+    static_assert(kElems * NT == BX * BK, "tile must split evenly over lanes");
     static_assert(kNV * kVec == kElems, "vector loads must split evenly");
 
     float r[kElems];
@@ -57,7 +57,7 @@ struct TileStage {
 
     // Coordinates (x, k) inside the tile of the first element of load v.
     __device__ static void coords(int tid, int v, int& x, int& k) {
-        const int f = tid + kThreads * v;
+        const int f = tid + NT * v;
         if constexpr (LAY == LAY_KC) {         // 4 consecutive k of one row
             x = f / (BK / 4);
             k = (f % (BK / 4)) * 4;
@@ -141,35 +141,47 @@ struct TileStage {
 
 // ---------------------------------------------------------------------------
 // Workgroup -> (tile row, tile column).  Any bijection is correct; these
-// orders only change cache reuse.
-__device__ __forceinline__ void tile_of_block(int order, int tiles_m, int tiles_n, int& tm,
-                                              int& tn) {
-    int w = static_cast<int>(blockIdx.x);
-    if (order == ORDER_ROW) {
-        tm = w / tiles_n;
-        tn = w % tiles_n;
+// orders only change cache reuse.  Divisions by runtime sizes use the
+// host-computed multiply-shift constants of TileGrid (integer only).
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+    return static_cast<uint32_t>((static_cast<uint64_t>(n) * f.m) >> f.s);
+}
+
+__device__ __forceinline__ void tile_of_block(const TileGrid& g, int& tm, int& tn) {
+    const uint32_t w = blockIdx.x;
+    if (g.order == ORDER_ROW) {
+        const uint32_t q = fdiv(w, g.div_n);
+        tm = static_cast<int>(q);
+        tn = static_cast<int>(w - q * g.div_n.d);
         return;
     }
-    if (order == ORDER_COL) {
-        tn = w / tiles_m;
-        tm = w % tiles_m;
+    if (g.order == ORDER_COL) {
+        const uint32_t q = fdiv(w, g.div_m);
+        tn = static_cast<int>(q);
+        tm = static_cast<int>(w - q * g.div_m.d);
         return;
     }
     // Workgroups are dealt round-robin to the 8 XCDs, each with its own L2.
     // Give XCD x the contiguous tile range [x*per, (x+1)*per) so tiles that
     // share operand panels meet in one L2; the remainder keeps its identity.
-    const int total = tiles_m * tiles_n;
-    const int per = total / 8;
-    int t = w;
-    if (w < per * 8) t = (w % 8) * per + (w / 8);
-    // Then walk groups of 8 tile rows, tile rows fastest inside a group.
-    constexpr int kGroup = 8;
-    const int span = kGroup * tiles_n;
-    const int first_m = (t / span) * kGroup;
-    const int rows = min(tiles_m - first_m, kGroup);
-    const int local = t % span;
-    tm = first_m + local % rows;
-    tn = local / rows;
+    const uint32_t total = static_cast<uint32_t>(g.tiles_m) * static_cast<uint32_t>(g.tiles_n);
+    const uint32_t per = total >> 3;
+    uint32_t t = w;
+    if (w < (per << 3)) t = (w & 7) * per + (w >> 3);
+    // Then walk groups of 8 tile rows, tile rows fastest inside a group; the
+    // last group may have fewer rows.
+    const uint32_t group = fdiv(t, g.div_span);  // span = 8 * tiles_n
+    const uint32_t first_m = group << 3;
+    const uint32_t local = t - group * g.div_span.d;
+    uint32_t q;
+    if (first_m + 8 <= static_cast<uint32_t>(g.tiles_m)) {
+        q = local >> 3;
+        tm = static_cast<int>(first_m + (local & 7));
+    } else {  // rows = tiles_m - first_m = tiles_m % 8
+        q = fdiv(local, g.div_last);
+        tm = static_cast<int>(first_m + (local - q * g.div_last.d));
+    }
+    tn = static_cast<int>(q);
 }
 
 // The TM row operands and TN column operands of one k step, as float4 reads
@@ -228,8 +240,7 @@ __device__ __forceinline__ void lane_tile_steps(const float* as, const float* bs
 template <int BM, int BN, int BK, int TM, int TN, int LA, int LB>
 __global__ __launch_bounds__(kThreads) void repops_tiled_kernel(OperandView A, OperandView B,
                                                                 OutView C, int64_t M, int64_t N,
-                                                                int64_t K, int tiles_m,
-                                                                int tiles_n, int order) {
+                                                                int64_t K, TileGrid grid) {
     static_assert((BM / TM) * (BN / TN) == kThreads, "one lane per TM x TN block");
     static_assert(TM % 4 == 0 && TN % 4 == 0, "lane blocks are groups of 4");
     constexpr int RG = TM / 4, CG = TN / 4;
@@ -243,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void repops_tiled_kernel(OperandView A, O
     const int tx = tid % (BN / TN);
     const int ty = tid / (BN / TN);
     int tm, tn;
-    tile_of_block(order, tiles_m, tiles_n, tm, tn);
+    tile_of_block(grid, tm, tn);
     const int64_t m0 = static_cast<int64_t>(tm) * BM;
     const int64_t n0 = static_cast<int64_t>(tn) * BN;
 
@@ -325,13 +336,209 @@ __global__ __launch_bounds__(kThreads) void repops_tiled_kernel(OperandView A, O
 }
 
 // ---------------------------------------------------------------------------
+// Matrix-core products, VALU sums.
+//
+// v_mfma_f32_32x32x1_2b_f32 has an inner dimension of 1: with the addend C
+// set to +0 it returns, for each of its 2 x 32 x 32 outputs, the single
+// product a_i * b_j + 0 rounded once to binary32 -- the same bits as a
+// separately rounded binary32 multiply (gradual underflow, round to nearest
+// even), except that an exact -0 product comes back as +0.  That exception
+// cannot change a result: the running sum s starts at +0 and never becomes
+// -0, and s + (+0) == s + (-0) for every such s.  The matrix core therefore
+// forms the products of one k step while the VALU adds the previous step's
+// products into the accumulators, one v_add_f32 per multiply-accumulate, in
+// ascending k.  No sum is ever formed inside the matrix core.
+//
+// Wave layout: lane l feeds row l of a 64-row strip (block l/32 of the
+// instruction) and column l%32 of a 32-column block (the same column in both
+// halves of the wave).  Register v of lane l then holds output row
+// 32*(v/16) + 8*((v%16)/4) + 4*(l/32) + v%4 and column l%32.
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+
+__device__ __forceinline__ int mprod_row(int v, int lane) {
+    return 32 * (v >> 4) + 8 * ((v & 15) >> 2) + 4 * (lane >> 5) + (v & 3);
+}
+
+// BK ascending k steps for one wave: TN column blocks of 32.  as/bs point at
+// this lane's row / column in the k-major LDS tiles.  Operands are read one
+// step ahead.  PIPE == 2 also forms products one step ahead (the matrix
+// instruction for k+1 is issued before the adds of step k, two product
+// buffers); PIPE == 1 keeps one product buffer and relies on the other waves
+// of the SIMD to fill the wait, which halves the product registers and
+// raises occupancy.  The empty asm pins each step's adds before the next
+// step's LDS reads.
+template <int BK, int TN, int LDA, int LDB, int PIPE>
+__device__ __forceinline__ void mprod_tile_steps(const float* as, const float* bs,
+                                                 float (&acc)[TN][32]) {
+    const f32x32 zero = {};
+    if constexpr (PIPE == 2) {
+        f32x32 p[2][TN];
+        float a[2], b[2][TN];
+        a[0] = as[0];
+#pragma unroll
+        for (int t = 0; t < TN; ++t) b[0][t] = bs[t * 32];
+        if (BK > 1) {
+            a[1] = as[LDA];
+#pragma unroll
+            for (int t = 0; t < TN; ++t) b[1][t] = bs[LDB + t * 32];
+        }
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+            p[0][t] = __builtin_amdgcn_mfma_f32_32x32x1f32(a[0], b[0][t], zero, 0, 0, 0);
+#pragma unroll
+        for (int k = 0; k < BK; ++k) {
+            const int c = k & 1;
+            if (k + 1 < BK) {
+#pragma unroll
+                for (int t = 0; t < TN; ++t)
+                    p[c ^ 1][t] = __builtin_amdgcn_mfma_f32_32x32x1f32(a[c ^ 1], b[c ^ 1][t],
+                                                                       zero, 0, 0, 0);
+            }
+            if (k + 2 < BK) {
+                a[c] = as[(k + 2) * LDA];
+#pragma unroll
+                for (int t = 0; t < TN; ++t) b[c][t] = bs[(k + 2) * LDB + t * 32];
+            }
+#pragma unroll
+            for (int t = 0; t < TN; ++t)
+#pragma unroll
+                for (int v = 0; v < 32; ++v) acc[t][v] = add_rn(acc[t][v], p[c][t][v]);
+#pragma unroll
+            for (int t = 0; t < TN; ++t)
+#pragma unroll
+                for (int v = 0; v < 32; ++v) asm volatile("" : "+v"(acc[t][v]));
+            // Inside the step: matrix instructions, LDS reads, then the adds
+            // (which read products issued one step earlier).
+            __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1 + TN, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 32 * TN, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        float a[2], b[2][TN];
+        a[0] = as[0];
+#pragma unroll
+        for (int t = 0; t < TN; ++t) b[0][t] = bs[t * 32];
+#pragma unroll
+        for (int k = 0; k < BK; ++k) {
+            const int c = k & 1;
+            f32x32 p[TN];
+#pragma unroll
+            for (int t = 0; t < TN; ++t)
+                p[t] = __builtin_amdgcn_mfma_f32_32x32x1f32(a[c], b[c][t], zero, 0, 0, 0);
+            if (k + 1 < BK) {
+                a[c ^ 1] = as[(k + 1) * LDA];
+#pragma unroll
+                for (int t = 0; t < TN; ++t) b[c ^ 1][t] = bs[(k + 1) * LDB + t * 32];
+            }
+#pragma unroll
+            for (int t = 0; t < TN; ++t)
+#pragma unroll
+                for (int v = 0; v < 32; ++v) acc[t][v] = add_rn(acc[t][v], p[t][v]);
+#pragma unroll
+            for (int t = 0; t < TN; ++t)
+#pragma unroll
+                for (int v = 0; v < 32; ++v) asm volatile("" : "+v"(acc[t][v]));
+            __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1 + TN, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 32 * TN, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+template <int WAVES_M, int WAVES_N, int TN, int BK, int PIPE, int LA, int LB>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void repops_mprod_kernel(
+    OperandView A, OperandView B, OutView C, int64_t M, int64_t N, int64_t K, TileGrid grid) {
+    constexpr int NT = 64 * WAVES_M * WAVES_N;
+    constexpr int BM = 64 * WAVES_M, BN = 32 * TN * WAVES_N;
+    constexpr int LDA = BM + kPad, LDB = BN + kPad;
+
+    __shared__ __attribute__((aligned(16))) float As[2][BK * LDA];
+    __shared__ __attribute__((aligned(16))) float Bs[2][BK * LDB];
+
+    const int tid = static_cast<int>(threadIdx.x);
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+    int tm, tn;
+    tile_of_block(grid, tm, tn);
+    const int64_t m0 = static_cast<int64_t>(tm) * BM;
+    const int64_t n0 = static_cast<int64_t>(tn) * BN;
+
+    float acc[TN][32];
+#pragma unroll
+    for (int t = 0; t < TN; ++t)
+#pragma unroll
+        for (int v = 0; v < 32; ++v) acc[t][v] = 0.0f;  // s = +0
+
+    TileStage<BM, BK, LA, NT> sa;
+    TileStage<BN, BK, LB, NT> sb;
+    sa.init(A, m0, tid);
+    sb.init(B, n0, tid);
+    const int64_t nfull = K / BK;
+    const bool tail = (K % BK) != 0;
+    const int arow = wm * 64 + lane;
+    const int bcol = wn * 32 * TN + (lane & 31);
+    const float* as0 = &As[0][arow];
+    const float* bs0 = &Bs[0][bcol];
+    const float* as1 = &As[1][arow];
+    const float* bs1 = &Bs[1][bcol];
+
+    if (nfull > 0) {
+        sa.load_full();
+        sb.load_full();
+    } else {
+        sa.load_tail(0, K, A.s_k);
+        sb.load_tail(0, K, B.s_k);
+    }
+    sa.store(As[0], tid);
+    sb.store(Bs[0], tid);
+    __syncthreads();
+
+    const int64_t ktiles = nfull + (tail ? 1 : 0);
+    for (int64_t kt = 0; kt < ktiles; ++kt) {
+        const bool more = kt + 1 < ktiles;
+        if (kt + 1 < nfull) {
+            sa.load_full();
+            sb.load_full();
+        } else if (more) {
+            sa.load_tail(nfull * BK, K, A.s_k);
+            sb.load_tail(nfull * BK, K, B.s_k);
+        }
+        asm volatile("" ::: "memory");
+        const bool odd = (kt & 1) != 0;
+        mprod_tile_steps<BK, TN, LDA, LDB, PIPE>(odd ? as1 : as0, odd ? bs1 : bs0, acc);
+        asm volatile("" ::: "memory");
+        if (more) {
+            sa.store(odd ? As[0] : As[1], tid);
+            sb.store(odd ? Bs[0] : Bs[1], tid);
+        }
+        __syncthreads();
+    }
+
+    // Epilogue: for each register v, lanes 0-31 and 32-63 each write 32
+    // consecutive columns of one row.
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+        const int64_t j = n0 + wn * 32 * TN + t * 32 + (lane & 31);
+        if (j >= N) continue;
+#pragma unroll
+        for (int v = 0; v < 32; ++v) {
+            const int64_t i = m0 + wm * 64 + mprod_row(v, lane);
+            if (i < M) C.p[i * C.s_i + j * C.s_j] = acc[t][v];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // One lane per output, operands straight from global memory.  The plainest
 // GPU form of the definition; every other variant must match it bit for bit.
 __global__ __launch_bounds__(256) void repops_naive_kernel(OperandView A, OperandView B,
                                                           OutView C, int64_t M, int64_t N,
-                                                          int64_t K, int blocks_n) {
-    const int bx = static_cast<int>(blockIdx.x) % blocks_n;
-    const int by = static_cast<int>(blockIdx.x) / blocks_n;
+                                                          int64_t K, FastDiv blocks_n) {
+    const uint32_t by = fdiv(blockIdx.x, blocks_n);
+    const uint32_t bx = blockIdx.x - by * blocks_n.d;
     const int64_t i = static_cast<int64_t>(by) * 16 + threadIdx.x / 16;
     const int64_t j = static_cast<int64_t>(bx) * 16 + threadIdx.x % 16;
     if (i >= M || j >= N) return;
@@ -350,8 +557,7 @@ __global__ __launch_bounds__(256) void repops_fill_zero_kernel(OutView C, int64_
 }
 
 // ---------------------------------------------------------------------------
-using TiledFn = void (*)(OperandView, OperandView, OutView, int64_t, int64_t, int64_t, int, int,
-                         int);
+using TiledFn = void (*)(OperandView, OperandView, OutView, int64_t, int64_t, int64_t, TileGrid);
 
 template <int BM, int BN, int BK, int TM, int TN>
 struct CfgTable {
@@ -368,15 +574,83 @@ struct CfgTable {
     }
 };
 
+template <int WM, int WN, int TN, int BK, int PIPE>
+struct MprodTable {
+    template <int LA, int LB>
+    static constexpr TiledFn fn() { return &repops_mprod_kernel<WM, WN, TN, BK, PIPE, LA, LB>; }
+    static TiledFn get(int la, int lb) {
+        static const TiledFn t[LAY_COUNT][LAY_COUNT] = {
+            {fn<0, 0>(), fn<0, 1>(), fn<0, 2>()},
+            {fn<1, 0>(), fn<1, 1>(), fn<1, 2>()},
+            {fn<2, 0>(), fn<2, 1>(), fn<2, 2>()},
+        };
+        return t[la][lb];
+    }
+};
+
 }  // namespace
+
+FastDiv make_fastdiv(uint32_t d) {
+    // floor(n / d) == (n * m) >> s for 0 <= n < 2^31 when s = 31 + ceil(log2 d)
+    // and m = ceil(2^s / d): the error n*(m*d - 2^s)/(d*2^s) is below 1/d.
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d) ++l;
+    const uint32_t s = 31 + l;
+    const uint64_t m = ((uint64_t(1) << s) + d - 1) / d;
+    return FastDiv{d, static_cast<uint32_t>(m), s};
+}
+
+TileGrid make_tile_grid(int tiles_m, int tiles_n, int order) {
+    TileGrid g{};
+    g.tiles_m = tiles_m;
+    g.tiles_n = tiles_n;
+    g.order = order;
+    g.div_n = make_fastdiv(static_cast<uint32_t>(tiles_n));
+    g.div_m = make_fastdiv(static_cast<uint32_t>(tiles_m));
+    g.div_span = make_fastdiv(8u * static_cast<uint32_t>(tiles_n));
+    const uint32_t last = static_cast<uint32_t>(tiles_m) & 7u;
+    g.div_last = make_fastdiv(last ? last : 8u);
+    return g;
+}
 
 void tile_shape(int cfg, int* bm, int* bn) {
     switch (cfg) {
         case CFG_128x128: *bm = 128; *bn = 128; break;
         case CFG_64x64: *bm = 64; *bn = 64; break;
         case CFG_128x64: *bm = 128; *bn = 64; break;
-        default: *bm = 64; *bn = 128; break;
+        case CFG_64x128: *bm = 64; *bn = 128; break;
+        case MCFG_128x128_W4: *bm = 128; *bn = 128; break;
+        case MCFG_128x128_W8: *bm = 128; *bn = 128; break;
+        case MCFG_256x128_W8: *bm = 256; *bn = 128; break;
+        case MCFG_128x128_W8_P1: *bm = 128; *bn = 128; break;
+        case MCFG_128x128_W4_P1: *bm = 128; *bn = 128; break;
+        case MCFG_256x128_W8_P1: *bm = 256; *bn = 128; break;
+        default: *bm = 64; *bn = 64; break;  // MCFG_64x64_W2
     }
+}
+
+int launch_mprod(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, OutView C,
+                 int64_t M, int64_t N, int64_t K, int order, void* stream) {
+    int bm, bn;
+    tile_shape(cfg, &bm, &bn);
+    const int tiles_m = static_cast<int>((M + bm - 1) / bm);
+    const int tiles_n = static_cast<int>((N + bn - 1) / bn);
+    const dim3 grid(static_cast<unsigned>(tiles_m) * static_cast<unsigned>(tiles_n));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    TiledFn fn;
+    int threads;
+    switch (cfg) {
+        case MCFG_128x128_W4: fn = MprodTable<2, 2, 2, 16, 2>::get(lay_a, lay_b); threads = 256; break;
+        case MCFG_128x128_W8: fn = MprodTable<2, 4, 1, 16, 2>::get(lay_a, lay_b); threads = 512; break;
+        case MCFG_256x128_W8: fn = MprodTable<4, 2, 2, 16, 2>::get(lay_a, lay_b); threads = 512; break;
+        case MCFG_128x128_W8_P1: fn = MprodTable<2, 4, 1, 16, 1>::get(lay_a, lay_b); threads = 512; break;
+        case MCFG_128x128_W4_P1: fn = MprodTable<2, 2, 2, 16, 1>::get(lay_a, lay_b); threads = 256; break;
+        case MCFG_256x128_W8_P1: fn = MprodTable<4, 2, 2, 16, 1>::get(lay_a, lay_b); threads = 512; break;
+        default: fn = MprodTable<1, 2, 1, 16, 2>::get(lay_a, lay_b); threads = 128; break;
+    }
+    hipLaunchKernelGGL(fn, grid, dim3(threads), 0, s, A, B, C, M, N, K,
+                       make_tile_grid(tiles_m, tiles_n, order));
+    return static_cast<int>(hipGetLastError());
 }
 
 int launch_tiled(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, OutView C,
@@ -395,7 +669,8 @@ int launch_tiled(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, Ou
         case CFG_128x64: fn = CfgTable<128, 64, 16, 8, 4>::get(lay_a, lay_b); break;
         default: fn = CfgTable<64, 128, 16, 4, 8>::get(lay_a, lay_b); break;
     }
-    hipLaunchKernelGGL(fn, grid, block, 0, s, A, B, C, M, N, K, tiles_m, tiles_n, order);
+    hipLaunchKernelGGL(fn, grid, block, 0, s, A, B, C, M, N, K,
+                       make_tile_grid(tiles_m, tiles_n, order));
     return static_cast<int>(hipGetLastError());
 }
 
@@ -405,7 +680,8 @@ int launch_naive(OperandView A, OperandView B, OutView C, int64_t M, int64_t N, 
     const int blocks_m = static_cast<int>((M + 15) / 16);
     hipLaunchKernelGGL(repops_naive_kernel,
                        dim3(static_cast<unsigned>(blocks_m) * static_cast<unsigned>(blocks_n)),
-                       dim3(256), 0, static_cast<hipStream_t>(stream), A, B, C, M, N, K, blocks_n);
+                       dim3(256), 0, static_cast<hipStream_t>(stream), A, B, C, M, N, K,
+                       make_fastdiv(static_cast<uint32_t>(blocks_n)));
     return static_cast<int>(hipGetLastError());
 }
 
