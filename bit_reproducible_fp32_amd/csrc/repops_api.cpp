@@ -177,9 +177,11 @@ int classify(const OperandView& v, int64_t K) {
 
 int pick(const Problem& p) {
     static const int large = variant_index("mprod1_t128x128x16_w8_xcd");
-    static const int small = variant_index("mprod_t64x64x16_w2_row");
+    static const int small = variant_index("valu_t64x64x16_r4x4_row");
     const int64_t tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128);
-    // 256 CUs: 128x128 tiles when there are at least two per CU, else 64x64.
+    // 256 CUs: 128x128 product tiles when there are at least two per CU;
+    // below that the problem cannot fill the chip and the 64x64 VALU tiles
+    // (more workgroups, measured faster at 256^3 and 1024^3) win.
     return tiles >= 512 ? large : small;
 }
 
