@@ -48,6 +48,9 @@ const Variant kVariants[] = {
     {"mprod1_t128x128x16_w8_xcd", KIND_MPROD, MCFG_128x128_W8_P1, ORDER_XCD_GROUP},
     {"mprod1_t128x128x16_w4_xcd", KIND_MPROD, MCFG_128x128_W4_P1, ORDER_XCD_GROUP},
     {"mprod1_t256x128x16_w8_xcd", KIND_MPROD, MCFG_256x128_W8_P1, ORDER_XCD_GROUP},
+    {"mprod16_t128x128x32_w16_xcd", KIND_MPROD, M16CFG_128x128_W16, ORDER_XCD_GROUP},
+    {"mprod16_t128x64x32_w8_xcd", KIND_MPROD, M16CFG_128x64_W8, ORDER_XCD_GROUP},
+    {"mprod16_t128x128x16_w8_xcd", KIND_MPROD, M16CFG_128x128_W8, ORDER_XCD_GROUP},
 };
 constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVariants[0]));
 

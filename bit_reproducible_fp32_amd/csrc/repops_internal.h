@@ -47,6 +47,10 @@ enum TileCfg : int {
     MCFG_128x128_W8_P1 = 8,
     MCFG_128x128_W4_P1 = 9,
     MCFG_256x128_W8_P1 = 10,
+    // 16x16x1 four-block shape: waves of 64 rows x 16*TN columns.
+    M16CFG_128x128_W16 = 11,  // 2x8 waves, TN=1 (1024 lanes), BK=32
+    M16CFG_128x64_W8 = 12,    // 2x4 waves, TN=1, BK=32
+    M16CFG_128x128_W8 = 13,   // 2x4 waves, TN=2
 };
 
 // Workgroup -> output-tile traversal orders (never change a bit).

@@ -447,6 +447,135 @@ __device__ __forceinline__ void mprod_tile_steps(const float* as, const float* b
     }
 }
 
+// The same scheme with v_mfma_f32_16x16x1_4b_f32: four 16x16 blocks of
+// single products.  Lane l feeds row l of a 64-row strip (block l/16) and
+// column l%16 of a 16-column block (the same column in all four blocks);
+// register v of lane l then holds row 16*(v/4) + 4*((l%64)/16) + v%4 and
+// column l%16.  Half the registers of the 32x32 shape per wave, so more
+// waves fit on a SIMD.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ int mprod16_row(int v, int lane) {
+    return 16 * (v >> 2) + 4 * (lane >> 4) + (v & 3);
+}
+
+template <int BK, int TN, int LDA, int LDB>
+__device__ __forceinline__ void mprod16_tile_steps(const float* as, const float* bs,
+                                                   float (&acc)[TN][16]) {
+    const f32x16 zero = {};
+    float a[2], b[2][TN];
+    a[0] = as[0];
+#pragma unroll
+    for (int t = 0; t < TN; ++t) b[0][t] = bs[t * 16];
+#pragma unroll
+    for (int k = 0; k < BK; ++k) {
+        const int c = k & 1;
+        f32x16 p[TN];
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+            p[t] = __builtin_amdgcn_mfma_f32_16x16x1f32(a[c], b[c][t], zero, 0, 0, 0);
+        if (k + 1 < BK) {
+            a[c ^ 1] = as[(k + 1) * LDA];
+#pragma unroll
+            for (int t = 0; t < TN; ++t) b[c ^ 1][t] = bs[(k + 1) * LDB + t * 16];
+        }
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[t][v] = add_rn(acc[t][v], p[t][v]);
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) asm volatile("" : "+v"(acc[t][v]));
+        __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1 + TN, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 16 * TN, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <int WAVES_M, int WAVES_N, int TN, int BK, int LA, int LB>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void repops_mprod16_kernel(
+    OperandView A, OperandView B, OutView C, int64_t M, int64_t N, int64_t K, TileGrid grid) {
+    constexpr int NT = 64 * WAVES_M * WAVES_N;
+    constexpr int BM = 64 * WAVES_M, BN = 16 * TN * WAVES_N;
+    constexpr int LDA = BM + kPad, LDB = BN + kPad;
+
+    __shared__ __attribute__((aligned(16))) float As[2][BK * LDA];
+    __shared__ __attribute__((aligned(16))) float Bs[2][BK * LDB];
+
+    const int tid = static_cast<int>(threadIdx.x);
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+    int tm, tn;
+    tile_of_block(grid, tm, tn);
+    const int64_t m0 = static_cast<int64_t>(tm) * BM;
+    const int64_t n0 = static_cast<int64_t>(tn) * BN;
+
+    float acc[TN][16];
+#pragma unroll
+    for (int t = 0; t < TN; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[t][v] = 0.0f;  // s = +0
+
+    TileStage<BM, BK, LA, NT> sa;
+    TileStage<BN, BK, LB, NT> sb;
+    sa.init(A, m0, tid);
+    sb.init(B, n0, tid);
+    const int64_t nfull = K / BK;
+    const bool tail = (K % BK) != 0;
+    const int arow = wm * 64 + lane;
+    const int bcol = wn * 16 * TN + (lane & 15);
+    const float* as0 = &As[0][arow];
+    const float* bs0 = &Bs[0][bcol];
+    const float* as1 = &As[1][arow];
+    const float* bs1 = &Bs[1][bcol];
+
+    if (nfull > 0) {
+        sa.load_full();
+        sb.load_full();
+    } else {
+        sa.load_tail(0, K, A.s_k);
+        sb.load_tail(0, K, B.s_k);
+    }
+    sa.store(As[0], tid);
+    sb.store(Bs[0], tid);
+    __syncthreads();
+
+    const int64_t ktiles = nfull + (tail ? 1 : 0);
+    for (int64_t kt = 0; kt < ktiles; ++kt) {
+        const bool more = kt + 1 < ktiles;
+        if (kt + 1 < nfull) {
+            sa.load_full();
+            sb.load_full();
+        } else if (more) {
+            sa.load_tail(nfull * BK, K, A.s_k);
+            sb.load_tail(nfull * BK, K, B.s_k);
+        }
+        asm volatile("" ::: "memory");
+        const bool odd = (kt & 1) != 0;
+        mprod16_tile_steps<BK, TN, LDA, LDB>(odd ? as1 : as0, odd ? bs1 : bs0, acc);
+        asm volatile("" ::: "memory");
+        if (more) {
+            sa.store(odd ? As[0] : As[1], tid);
+            sb.store(odd ? Bs[0] : Bs[1], tid);
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+        const int64_t j = n0 + wn * 16 * TN + t * 16 + (lane & 15);
+        if (j >= N) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t i = m0 + wm * 64 + mprod16_row(v, lane);
+            if (i < M) C.p[i * C.s_i + j * C.s_j] = acc[t][v];
+        }
+    }
+}
+
 template <int WAVES_M, int WAVES_N, int TN, int BK, int PIPE, int LA, int LB>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void repops_mprod_kernel(
     OperandView A, OperandView B, OutView C, int64_t M, int64_t N, int64_t K, TileGrid grid) {
@@ -588,6 +717,20 @@ struct MprodTable {
     }
 };
 
+template <int WM, int WN, int TN, int BK>
+struct Mprod16Table {
+    template <int LA, int LB>
+    static constexpr TiledFn fn() { return &repops_mprod16_kernel<WM, WN, TN, BK, LA, LB>; }
+    static TiledFn get(int la, int lb) {
+        static const TiledFn t[LAY_COUNT][LAY_COUNT] = {
+            {fn<0, 0>(), fn<0, 1>(), fn<0, 2>()},
+            {fn<1, 0>(), fn<1, 1>(), fn<1, 2>()},
+            {fn<2, 0>(), fn<2, 1>(), fn<2, 2>()},
+        };
+        return t[la][lb];
+    }
+};
+
 }  // namespace
 
 FastDiv make_fastdiv(uint32_t d) {
@@ -625,6 +768,9 @@ void tile_shape(int cfg, int* bm, int* bn) {
         case MCFG_128x128_W8_P1: *bm = 128; *bn = 128; break;
         case MCFG_128x128_W4_P1: *bm = 128; *bn = 128; break;
         case MCFG_256x128_W8_P1: *bm = 256; *bn = 128; break;
+        case M16CFG_128x128_W16: *bm = 128; *bn = 128; break;
+        case M16CFG_128x64_W8: *bm = 128; *bn = 64; break;
+        case M16CFG_128x128_W8: *bm = 128; *bn = 128; break;
         default: *bm = 64; *bn = 64; break;  // MCFG_64x64_W2
     }
 }
@@ -646,6 +792,9 @@ int launch_mprod(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, Ou
         case MCFG_128x128_W8_P1: fn = MprodTable<2, 4, 1, 16, 1>::get(lay_a, lay_b); threads = 512; break;
         case MCFG_128x128_W4_P1: fn = MprodTable<2, 2, 2, 16, 1>::get(lay_a, lay_b); threads = 256; break;
         case MCFG_256x128_W8_P1: fn = MprodTable<4, 2, 2, 16, 1>::get(lay_a, lay_b); threads = 512; break;
+        case M16CFG_128x128_W16: fn = Mprod16Table<2, 8, 1, 32>::get(lay_a, lay_b); threads = 1024; break;
+        case M16CFG_128x64_W8: fn = Mprod16Table<2, 4, 1, 32>::get(lay_a, lay_b); threads = 512; break;
+        case M16CFG_128x128_W8: fn = Mprod16Table<2, 4, 2, 16>::get(lay_a, lay_b); threads = 512; break;
         default: fn = MprodTable<1, 2, 1, 16, 2>::get(lay_a, lay_b); threads = 128; break;
     }
     hipLaunchKernelGGL(fn, grid, dim3(threads), 0, s, A, B, C, M, N, K,

@@ -182,22 +182,24 @@ def test_isa_valu_kernels_use_no_matrix_instructions():
             assert not MATRIX.search(body), name
 
 
+# FP32 matrix shapes with inner dimension 1: every output is one product.
+K1_FP32_SHAPES = {"v_mfma_f32_32x32x1_2b_f32", "v_mfma_f32_16x16x1_4b_f32",
+                  "v_mfma_f32_4x4x1_16b_f32"}
 MFMA_LINE = re.compile(r"^\s+(v_mfma\w*)\s+([^\n]*)$", re.M)
 
 
 def test_isa_matrix_product_kernels_only_form_single_products():
-    """The product kernels may use exactly one matrix instruction: the FP32
-    shape with inner dimension 1 (no sum inside the matrix core), with the
-    addend operand the literal 0, and every product must be followed by VALU
-    adds (the fixed-order sum)."""
+    """The product kernels may use only FP32 matrix shapes with inner
+    dimension 1 (no sum inside the matrix core), with the addend operand the
+    literal 0, no VALU multiply, and VALU adds (the fixed-order sum)."""
     bodies, _ = kernels()
-    mprod = {n: b for n, b in bodies.items() if "mprod_kernel" in n}
-    assert mprod
+    mprod = {n: b for n, b in bodies.items() if re.search(r"mprod(16)?_kernel", n)}
+    assert len(mprod) >= 2
     for name, body in mprod.items():
         found = MFMA_LINE.findall(body)
         assert found, name
         for mnem, ops in found:
-            assert mnem == "v_mfma_f32_32x32x1_2b_f32", (name, mnem)
+            assert mnem in K1_FP32_SHAPES, (name, mnem)
             assert ops.split(",")[-1].strip() == "0", (name, ops)
         assert "v_add_f32" in body and "v_mul_f32" not in body, name
 
