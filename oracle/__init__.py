@@ -30,7 +30,7 @@ import subprocess
 import numpy as np
 
 from .emulate import emulate_f64  # noqa: F401
-from .exact import exact_matmul, round_binary32  # noqa: F401
+from .exact import exact_fold_mean_sgd, exact_matmul, round_binary32  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "repops_oracle.c")
@@ -68,6 +68,8 @@ def _load():
         lib.repops_oracle_entries_f32.argtypes = [
             fp, i64, i64, fp, i64, i64, i64, i64, i64, ip, ip, fp, fp, i64, fp, ip]
         lib.repops_oracle_entries_f32.restype = ip
+        lib.repops_oracle_fold_mean_sgd_f32.argtypes = [fp, i64, i64, ctypes.c_float, fp, fp, fp]
+        lib.repops_oracle_fold_mean_sgd_f32.restype = ip
         lib.repops_oracle_env_status.argtypes = []
         lib.repops_oracle_env_status.restype = ip
         _lib = lib
@@ -149,3 +151,37 @@ def entries_f32(A: np.ndarray, B: np.ndarray, ii, jj, trans_a: bool = False,
     if rc != 0:
         raise RuntimeError("oracle failed with status %d" % rc)
     return out
+
+
+def canonical_order(dids) -> list:
+    """Contributor indices sorted by DID byte order (Zoo Per-LLM Chain
+    Soundness, "Ordering subroutine": lexicographic on the DID bytes).
+    Python compares bytes objects exactly that way (unsigned bytes, a proper
+    prefix first).  Two equal DIDs are an error: the batch is keyed by
+    contributor."""
+    keys = [bytes(x) for x in dids]
+    if len(set(keys)) != len(keys):
+        raise ValueError("duplicate contributor DID")
+    return sorted(range(len(keys)), key=lambda c: keys[c])
+
+
+def fold_mean_sgd_f32(grads, eta, theta):
+    """Left-fold average of the gradients (in the given order), then
+    theta - eta * gbar; returns (new theta, gbar) as float32 arrays."""
+    grads = [np.ascontiguousarray(g, dtype=np.float32) for g in grads]
+    theta = np.ascontiguousarray(theta, dtype=np.float32)
+    k = len(grads)
+    if k < 1:
+        raise ValueError("need at least one gradient")
+    d = theta.shape[0]
+    if any(g.shape != (d,) for g in grads):
+        raise ValueError("gradients and theta must all have length d")
+    ptrs = (ctypes.c_void_p * k)(*[g.ctypes.data for g in grads])
+    out = np.empty(d, np.float32)
+    gbar = np.empty(d, np.float32)
+    rc = _load().repops_oracle_fold_mean_sgd_f32(ptrs, k, d, float(np.float32(eta)),
+                                                theta.ctypes.data, out.ctypes.data,
+                                                gbar.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle failed with status %d" % rc)
+    return out, gbar

@@ -127,3 +127,32 @@ def exact_matmul(A: np.ndarray, B: np.ndarray, trans_a: bool = False,
                 s = exact_add(s, exact_mul(a[i][k], b[k][j]))
             out[i, j] = encode(s)
     return out.view(np.float32)
+
+
+def exact_neg(x):
+    return x if x[0] == "nan" else (x[0], 1 - x[1], x[2])
+
+
+def exact_fold_mean_sgd(G: np.ndarray, eta, theta: np.ndarray):
+    """Left-fold average and SGD step by exact arithmetic (Zoo Per-LLM Chain
+    Soundness, "Detailed proof: deterministic ordering"): S = left fold of the
+    rows of G (k x d) in row order, gbar = RN(RN(1/k) * S),
+    theta' = RN(theta - RN(eta * gbar)).  Returns (theta', gbar) float32."""
+    G = np.asarray(G, dtype=np.float32)
+    k, d = G.shape
+    gbits = np.ascontiguousarray(G).view(np.uint32)
+    tbits = np.ascontiguousarray(np.asarray(theta, dtype=np.float32)).view(np.uint32)
+    ebits = int(np.array([eta], dtype=np.float32).view(np.uint32)[0])
+    inv_k = decode_binary32(round_binary32(0, Fraction(1, k)))
+    e = decode_binary32(ebits)
+    out = np.empty(d, dtype=np.uint32)
+    gbar = np.empty(d, dtype=np.uint32)
+    for j in range(d):
+        s = decode_binary32(int(gbits[0, j]))
+        for c in range(1, k):
+            s = exact_add(s, decode_binary32(int(gbits[c, j])))
+        gb = exact_mul(inv_k, s)
+        gbar[j] = encode(gb)
+        step = exact_mul(e, gb)
+        out[j] = encode(exact_add(decode_binary32(int(tbits[j])), exact_neg(step)))
+    return out.view(np.float32), gbar.view(np.float32)

@@ -183,3 +183,39 @@ int repops_oracle_entries_f32(const float *A, int64_t a_rs, int64_t a_cs,
                        trans_a, trans_b, ii, jj, out, 0, 0};
     return run_split(base, count, nthreads);
 }
+
+/*
+ * Fixed-order average of k contributor gradients and the SGD step, element
+ * by element (Zoo Per-LLM Chain Soundness, "Detailed proof: deterministic
+ * ordering": paragraphs "Ordering subroutine", "Determinism of left-fold"
+ * and "Update step"):
+ *
+ *     S     = (((g_0 + g_1) + g_2) + ...) + g_{k-1}   left fold, in the given
+ *                                                      (canonical) order
+ *     gbar  = (1/k) * S
+ *     theta = theta - eta * gbar
+ *
+ * Readings: every operation is a separately rounded binary32 operation
+ * (round-to-nearest-even, no fused multiply-add, as the spec's kernel
+ * manifest pins); "(1/k) *" is the binary32 quotient 1/k, rounded once, times
+ * S; the fold starts from g_0 itself (no +0 in front).  grads[c] points at d
+ * floats of contributor c, already in fold order.  theta_out may equal
+ * theta_in; gbar_out may be NULL.  Returns 0, -1 for bad sizes, -2 for a
+ * floating-point environment that is not RNE with gradual underflow.
+ */
+int repops_oracle_fold_mean_sgd_f32(const float *const *grads, int64_t k, int64_t d, float eta,
+                                    const float *theta_in, float *theta_out, float *gbar_out)
+{
+    if (k < 1 || d < 0) return -1;
+    if (repops_oracle_env_status() != 0) return -2;
+    const float inv_k = 1.0f / (float)k;
+    for (int64_t e = 0; e < d; ++e) {
+        float s = grads[0][e];
+        for (int64_t c = 1; c < k; ++c) s = s + grads[c][e];
+        const float gbar = inv_k * s;
+        if (gbar_out) gbar_out[e] = gbar;
+        const float step = eta * gbar;
+        theta_out[e] = theta_in[e] - step;
+    }
+    return 0;
+}
