@@ -102,7 +102,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama8b_mlp_up")
+    ap.add_argument("--workload", default="llama8b_mlp_up",
+                    help="a matmul workload (default: the Llama-8B up-projection) or a "
+                         "fold workload (fixed-order gradient average + SGD step)")
     ap.add_argument("--variant", default=None, help="force a kernel variant (name or index)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -126,6 +128,8 @@ def main():
         sys.exit(1)
     rp.load()  # raises if the HIP library is not built
     dev = torch.device("cuda:0")
+    if args.workload in inputs.FOLD_WORKLOADS:
+        return bench_fold(args, torch, rp, inputs, dev)
     w = inputs.WORKLOADS[args.workload]
     log("workload %s: %s" % (w.name, w.description))
     A, B = inputs.make_operands(w.name)
@@ -255,6 +259,92 @@ def main():
                       "min": round(min(kernel_ms), 4), "max": round(max(kernel_ms), 4)},
     }
     rec.update(extra)
+    print(json.dumps(rec), flush=True)
+
+
+HBM_PEAK_GBS = 8000.0
+FOLD_KERNEL_SRC = os.path.join(ROOT, "bit_reproducible_fp32_amd", "csrc", "repops_fold.hip")
+FOLD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fold_k8_d64M_traffic.txt")
+
+
+def bench_fold(args, torch, rp, inputs, dev):
+    """Fixed-order gradient average + SGD step: one step = one C-ABI call on
+    k resident gradients and theta (gbar not written).  value = algorithmic
+    GB/s = 4*d*(k+2) bytes / time; roofline bound hbm against 8 TB/s."""
+    import oracle
+    w = inputs.FOLD_WORKLOADS[args.workload]
+    log("fold workload %s: %s" % (w.name, w.description))
+    grads, theta = inputs.make_fold_operands(w.name)
+    gg = [torch.from_numpy(g).to(dev) for g in grads]
+    th0 = torch.from_numpy(theta).to(dev)
+    th = th0.clone()
+    stream = torch.cuda.current_stream(dev)
+    eta = np.float32(w.eta)
+
+    def step():
+        rp.fold_mean_sgd(gg, th, eta, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        starts[s].record(stream)
+        step()
+        ends[s].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [starts[s].elapsed_time(ends[s]) for s in range(args.steps)]
+    log("per-step kernel ms: " + " ".join("%.4f" % t for t in kernel_ms))
+    nbytes = float(w.algorithmic_bytes)
+    ms_per_step = wall * 1e3 / args.steps
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    k_avg = float(np.mean(kernel_ms))
+    achieved = nbytes / (k_avg * 1e-3) / 1e9
+
+    # Bit-exactness gate: one step from the initial theta, sampled parameters.
+    th.copy_(th0)
+    step()
+    torch.cuda.synchronize()
+    idx = inputs.fold_sample_indices(w.d, 4096, 99)
+    want, _ = oracle.fold_mean_sgd_f32([g[idx] for g in grads], eta, theta[idx])
+    got = th.cpu().numpy()[idx]
+    if not np.array_equal(got.view(np.uint32), want.view(np.uint32)):
+        print("bench.py: fold output differs from the oracle; no number is reported",
+              file=sys.stderr)
+        sys.exit(3)
+    log("bit-exact on %d sampled parameters" % idx.size)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        oracle.fold_mean_sgd_f32(grads, eta, theta)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": "the whole workload (k=%d, d=%d) in %.1f s, single thread" % (w.k, w.d, dt)}
+
+    traffic = None
+    if os.path.exists(FOLD_TRAFFIC_FILE):
+        fields = dict(re.findall(r"^([a-z_0-9]+):\s*(\S+)\s*$", open(FOLD_TRAFFIC_FILE).read(), re.M))
+        if fields.get("kernel_source_sha256") == hashlib.sha256(
+                open(FOLD_KERNEL_SRC, "rb").read()).hexdigest():
+            traffic = float(fields.get("traffic_bytes_per_launch", "nan"))
+    rec = {
+        "metric": "fixed-order gradient average + SGD step, algorithmic GB/s, bit-exact",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "strong", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded numpy PCG64)",
+        "config": {"workload": "%s k=%d d=%d" % (w.name, w.k, w.d), "k": w.k, "d": w.d},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu, "bitexact_sampled": True,
+        "kernel_ms": {"mean": round(k_avg, 5), "median": round(float(np.median(kernel_ms)), 5),
+                      "min": round(min(kernel_ms), 5), "max": round(max(kernel_ms), 5)},
+    }
     print(json.dumps(rec), flush=True)
 
 

@@ -18,6 +18,8 @@ from ._lib import (  # noqa: F401
     EXPORTS,
     REPOPS_ERR_ALIAS,
     REPOPS_ERR_DIM,
+    REPOPS_ERR_DUPLICATE,
+    REPOPS_FOLD_MAX_PER_PASS,
     REPOPS_ERR_HIP,
     REPOPS_ERR_NULL,
     REPOPS_ERR_STRIDE,
@@ -26,7 +28,9 @@ from ._lib import (  # noqa: F401
     RepopsError,
     load,
     repops_build_manifest,
+    repops_canonical_order,
     repops_check_args_f32,
+    repops_fold_mean_sgd_f32,
     repops_matmul_f32,
     repops_matmul_f32_ex,
     repops_pick_variant_f32,
@@ -90,3 +94,55 @@ def matmul(a, b, *, trans_a: bool = False, trans_b: bool = False, out=None, vari
     if st != REPOPS_OK:
         raise RepopsError(st, "repops_matmul_f32")
     return out
+
+
+def canonical_order(dids):
+    """Contributor indices in byte-lexicographic order of their identities
+    (bytes or str), computed by the library; raises on duplicates."""
+    st, order = repops_canonical_order([d.encode() if isinstance(d, str) else bytes(d)
+                                        for d in dids])
+    if st != REPOPS_OK:
+        raise RepopsError(st, "repops_canonical_order")
+    return order
+
+
+def fold_mean_sgd(grads, theta, eta, *, dids=None, gbar=None, stream=None):
+    """Fixed-order gradient average and SGD step on the GPU, bit-reproducible.
+
+    ``grads``: list of k contiguous 1-D float32 CUDA tensors of length d (one
+    per contributor); when ``dids`` (their identities) is given they are
+    folded in canonical DID order, else in list order.  ``theta`` (d float32,
+    contiguous) is updated in place: theta -= eta * gbar with
+    gbar = RN(1/k) * (((g_1 + g_2) + ...) + g_k).  ``gbar``: optional output
+    tensor (required when k > REPOPS_FOLD_MAX_PER_PASS).  Returns gbar.
+    """
+    import numpy as np
+    import torch
+
+    k = len(grads)
+    if k < 1:
+        raise ValueError("need at least one gradient")
+    if dids is not None:
+        if len(dids) != k:
+            raise ValueError("one identity per gradient")
+        grads = [grads[c] for c in canonical_order(dids)]
+    d = theta.numel()
+    for t in list(grads) + [theta] + ([gbar] if gbar is not None else []):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32:
+            raise TypeError("gradients, theta and gbar must be float32 tensors")
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a GPU; this library has no CPU path")
+        if not t.is_contiguous() or t.numel() != d:
+            raise ValueError("every tensor must be contiguous with d = %d elements" % d)
+    if gbar is None and k > REPOPS_FOLD_MAX_PER_PASS:
+        gbar = torch.empty_like(theta)
+    if stream is None:
+        stream = torch.cuda.current_stream(theta.device)
+    with torch.cuda.device(theta.device):
+        st = repops_fold_mean_sgd_f32([g.data_ptr() for g in grads], k, d,
+                                      float(np.float32(eta)), theta.data_ptr(),
+                                      gbar.data_ptr() if gbar is not None else None,
+                                      stream.cuda_stream)
+    if st != REPOPS_OK:
+        raise RepopsError(st, "repops_fold_mean_sgd_f32")
+    return gbar

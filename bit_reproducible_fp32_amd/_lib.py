@@ -19,6 +19,8 @@ REPOPS_ERR_STRIDE = 3
 REPOPS_ERR_ALIAS = 4
 REPOPS_ERR_VARIANT = 5
 REPOPS_ERR_HIP = 6
+REPOPS_ERR_DUPLICATE = 7
+REPOPS_FOLD_MAX_PER_PASS = 64
 
 EXPORTS = (
     "repops_matmul_f32",
@@ -29,6 +31,8 @@ EXPORTS = (
     "repops_variant_name",
     "repops_strerror",
     "repops_build_manifest",
+    "repops_canonical_order",
+    "repops_fold_mean_sgd_f32",
 )
 
 _lib = None
@@ -68,6 +72,10 @@ def load():
     lib.repops_strerror.restype = cp
     lib.repops_build_manifest.argtypes = []
     lib.repops_build_manifest.restype = cp
+    lib.repops_canonical_order.argtypes = [vp, vp, i64, vp]
+    lib.repops_canonical_order.restype = ci
+    lib.repops_fold_mean_sgd_f32.argtypes = [vp, i64, i64, ctypes.c_float, vp, vp, vp]
+    lib.repops_fold_mean_sgd_f32.restype = ci
     _lib = lib
     return lib
 
@@ -110,6 +118,27 @@ def repops_strerror(status: int) -> str:
 
 def repops_build_manifest() -> str:
     return load().repops_build_manifest().decode()
+
+
+def repops_canonical_order(dids):
+    """(status, order): order[r] is the index of the contributor at rank r
+    in byte-lexicographic order of the identities (bytes objects)."""
+    k = len(dids)
+    bufs = [bytes(x) for x in dids]
+    ptrs = (ctypes.c_char_p * max(k, 1))(*bufs)
+    lens = (ctypes.c_int64 * max(k, 1))(*[len(b) for b in bufs])
+    out = (ctypes.c_int64 * max(k, 1))()
+    st = load().repops_canonical_order(ctypes.cast(ptrs, ctypes.c_void_p),
+                                       ctypes.cast(lens, ctypes.c_void_p), k,
+                                       ctypes.cast(out, ctypes.c_void_p))
+    return st, [int(out[r]) for r in range(k)]
+
+
+def repops_fold_mean_sgd_f32(grads, k, d, eta, theta, gbar, stream) -> int:
+    """grads: sequence of k device addresses (ints), in fold order."""
+    arr = (ctypes.c_void_p * max(int(k), 1))(*[int(g) for g in grads])
+    return load().repops_fold_mean_sgd_f32(ctypes.cast(arr, ctypes.c_void_p), int(k), int(d),
+                                           float(eta), theta, gbar, stream)
 
 
 strerror = repops_strerror

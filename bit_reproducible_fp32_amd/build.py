@@ -24,7 +24,9 @@ ASM = os.path.join(HERE, "librepops_gfx950.s")
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = [os.path.join(CSRC, "repops_kernels.hip"), os.path.join(CSRC, "repops_api.cpp")]
+KERNEL_SOURCES = [os.path.join(CSRC, "repops_kernels.hip"), os.path.join(CSRC, "repops_fold.hip")]
+SOURCES = KERNEL_SOURCES + [os.path.join(CSRC, "repops_api.cpp"),
+                            os.path.join(CSRC, "repops_fold_api.cpp")]
 
 FP_FLAGS = ["-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero"]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -49,12 +51,18 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
-    # Device-only assembly of the kernels, for the instruction scan.
-    asm_tmp = ASM + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *COMMON, *FP_FLAGS, *DEVICE_FLAGS, "--cuda-device-only", "-S",
-           "-o", asm_tmp, SOURCES[0]]
-    subprocess.run(cmd, check=True)
-    os.replace(asm_tmp, ASM)
+    # Device-only assembly of every kernel source, for the instruction scan.
+    parts = []
+    for src in KERNEL_SOURCES:
+        asm_tmp = ASM + ".tmp%d" % os.getpid()
+        cmd = [HIPCC, *COMMON, *FP_FLAGS, *DEVICE_FLAGS, "--cuda-device-only", "-S",
+               "-o", asm_tmp, src]
+        subprocess.run(cmd, check=True)
+        parts.append(open(asm_tmp).read())
+        os.remove(asm_tmp)
+    with open(ASM + ".tmp", "w") as f:
+        f.write("\n".join(parts))
+    os.replace(ASM + ".tmp", ASM)
     return LIB
 
 

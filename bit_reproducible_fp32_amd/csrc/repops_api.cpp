@@ -270,6 +270,7 @@ const char* repops_strerror(repops_status status) {
         case REPOPS_ERR_ALIAS: return "output overlaps an input";
         case REPOPS_ERR_VARIANT: return "unknown kernel variant";
         case REPOPS_ERR_HIP: return "HIP launch error";
+        case REPOPS_ERR_DUPLICATE: return "two contributors share one identity";
     }
     return "unknown status";
 }

@@ -86,4 +86,14 @@ int launch_naive(OperandView A, OperandView B, OutView C, int64_t M, int64_t N, 
                  void* stream);
 int launch_fill_zero(OutView C, int64_t M, int64_t N, void* stream);
 
+// Fixed-order gradient fold: the contributors one pass reads, in fold order.
+constexpr int kFoldMax = 64;
+struct FoldArgs {
+    const float* g[kFoldMax];
+};
+
+// One pass of the fold over n <= kFoldMax contributors (see repops_fold.hip).
+int launch_fold(const FoldArgs& G, int n, bool first, bool last, float* sum, float* theta,
+                float* gbar, float inv_k, float eta, int64_t d, bool vec, void* stream);
+
 }  // namespace repops

@@ -127,3 +127,52 @@ def sample_entries(M: int, N: int, count: int, seed: int):
     ii += list(rng.integers(0, M, size=count))
     jj += list(rng.integers(0, N, size=count))
     return np.asarray(ii, dtype=np.int64), np.asarray(jj, dtype=np.int64)
+
+
+@dataclass(frozen=True)
+class FoldWorkload:
+    """Fixed-order gradient average + SGD step over d parameters from k
+    contributors (the chain-soundness spec's aggregation, synthetic data)."""
+    name: str
+    k: int
+    d: int
+    grad_std: str
+    theta_std: str
+    eta: float
+    seed: int
+    description: str
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """k gradients and theta read, theta written (gbar not written)."""
+        return 4 * self.d * (self.k + 2)
+
+
+FOLD_WORKLOADS = {
+    w.name: w
+    for w in [
+        FoldWorkload("fold_k8_d64M", 8, 1 << 26, "normal0.001", "normal0.02", 1e-3, 6001,
+                     "k=8 contributors, d=2^26 parameters (67M, a 268 MB gradient each), "
+                     "gradients ~ N(0, 0.001), theta ~ N(0, 0.02), eta = 1e-3"),
+        FoldWorkload("fold_k3_d1M", 3, (1 << 20) + 7, "normal0.001", "normal0.02", 1e-3, 6101,
+                     "k=3 (1/k inexact), d=2^20+7 (ragged tail)"),
+    ]
+}
+
+
+def make_fold_operands(name: str):
+    """(list of k gradient arrays, theta) as float32, in contributor order
+    c = 0..k-1 (seeds seed+1+c for the gradients, seed for theta)."""
+    w = FOLD_WORKLOADS[name]
+    grads = [_draw(w.grad_std, (w.d,), w.seed + 1 + c) for c in range(w.k)]
+    theta = _draw(w.theta_std, (w.d,), w.seed)
+    return grads, theta
+
+
+def fold_sample_indices(d: int, count: int, seed: int):
+    """Parameters to check at full size: both ends, a window around every
+    multiple of 4 boundary class, and count uniform random indices."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    idx = list(range(min(d, 64))) + list(range(max(0, d - 64), d))
+    idx += list(rng.integers(0, d, size=count))
+    return np.unique(np.asarray(idx, dtype=np.int64))

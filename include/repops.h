@@ -57,7 +57,8 @@ typedef enum repops_status {
                                outputs to one element */
     REPOPS_ERR_ALIAS = 4,   /* the bytes C spans overlap those of A or B */
     REPOPS_ERR_VARIANT = 5, /* unknown variant index */
-    REPOPS_ERR_HIP = 6      /* the HIP runtime reported an error at launch */
+    REPOPS_ERR_HIP = 6,     /* the HIP runtime reported an error at launch */
+    REPOPS_ERR_DUPLICATE = 7 /* two contributors share one identity */
 } repops_status;
 
 /*
@@ -122,6 +123,55 @@ const char* repops_strerror(repops_status status);
  * exactly which kernels produced them.
  */
 const char* repops_build_manifest(void);
+
+/* ------------------------------------------------------------------------
+ * Fixed-order gradient average and SGD step (Zoo Per-LLM Chain Soundness,
+ * section "Detailed proof: deterministic ordering", paragraphs "Ordering
+ * subroutine", "Determinism of left-fold" and "Update step"; the aggregation
+ * rule and the order lemma of section "Deterministic gradient ordering").
+ * ---------------------------------------------------------------------- */
+
+/* Contributors one pass of the fold kernel reads; longer folds run in several
+ * passes that carry the running sum through `gbar`. */
+#define REPOPS_FOLD_MAX_PER_PASS 64
+
+/*
+ * Canonical contributor order: the k contributors sorted lexicographically by
+ * the bytes of their identities (unsigned byte comparison; a proper prefix
+ * sorts first).  dids[c] points at did_lens[c] bytes (may be NULL when the
+ * length is 0).  On success order_out[r] is the index c of the contributor
+ * at rank r.  Host only; touches no device.
+ * Errors: REPOPS_ERR_NULL (NULL array with k > 0, or NULL bytes with a
+ * nonzero length), REPOPS_ERR_DIM (k < 0 or a negative length),
+ * REPOPS_ERR_DUPLICATE (two identical identities: the batch is keyed by
+ * contributor).  order_out is unspecified after an error.
+ */
+repops_status repops_canonical_order(const uint8_t* const* dids, const int64_t* did_lens,
+                                     int64_t k, int64_t* order_out);
+
+/*
+ * For every parameter e in [0, d), with contributors in the order given:
+ *     S        = (((g_0[e] + g_1[e]) + g_2[e]) + ...) + g_{k-1}[e]
+ *     gbar[e]  = RN(RN(1/k) * S)
+ *     theta[e] = RN(theta[e] - RN(eta * gbar[e]))
+ * each operation a separately rounded binary32 operation (round to nearest
+ * even, gradual underflow, no fused multiply-add).  The fold starts from
+ * g_0 itself; "(1/k) *" is the binary32 quotient 1/k rounded once, then a
+ * multiply.  Bits never depend on launch shape or pointer alignment.
+ *
+ * grads: host array of k device pointers, already in canonical order (see
+ * repops_canonical_order), each to d contiguous floats.  theta: device, d
+ * floats, updated in place.  gbar: device, d floats, receives gbar; may be
+ * NULL when k <= REPOPS_FOLD_MAX_PER_PASS, required above that (it holds the
+ * running sum between passes).  Queued on `stream` (a hipStream_t as void*).
+ * The grads array itself is read before the call returns; the gradients are
+ * borrowed until the queued work completes.
+ * Errors: REPOPS_ERR_NULL, REPOPS_ERR_DIM (k < 1, k > 2^24, d < 0, or an
+ * offset overflow), REPOPS_ERR_ALIAS (theta or gbar overlaps a gradient, or
+ * gbar overlaps theta), REPOPS_ERR_HIP.  d == 0 is a successful no-op.
+ */
+repops_status repops_fold_mean_sgd_f32(const float* const* grads, int64_t k, int64_t d,
+                                       float eta, float* theta, float* gbar, void* stream);
 
 #ifdef __cplusplus
 }

@@ -133,8 +133,8 @@ def test_pick_variant():
 
 
 def test_strerror_and_manifest():
-    for st in range(7):
-        assert rp.repops_strerror(st)
+    for st in range(8):
+        assert rp.repops_strerror(st) != "unknown status"
     assert rp.repops_strerror(99) == "unknown status"
     man = json.loads(rp.repops_build_manifest())
     assert man["offload_arch"] == "gfx950"
