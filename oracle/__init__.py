@@ -30,7 +30,8 @@ import subprocess
 import numpy as np
 
 from .emulate import emulate_f64  # noqa: F401
-from .exact import exact_fold_mean_sgd, exact_matmul, round_binary32  # noqa: F401
+from .exact import (exact_fold_mean_sgd, exact_matmul, exact_matmul_bias,  # noqa: F401
+                    round_binary32)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "repops_oracle.c")
@@ -70,6 +71,10 @@ def _load():
         lib.repops_oracle_entries_f32.restype = ip
         lib.repops_oracle_fold_mean_sgd_f32.argtypes = [fp, i64, i64, ctypes.c_float, fp, fp, fp]
         lib.repops_oracle_fold_mean_sgd_f32.restype = ip
+        lib.repops_oracle_matmul_batched_f32.argtypes = [
+            fp, i64, i64, i64, fp, i64, i64, i64, fp, i64, i64, i64, i64, i64, i64, i64,
+            ip, ip, fp, i64, i64, ip]
+        lib.repops_oracle_matmul_batched_f32.restype = ip
         lib.repops_oracle_env_status.argtypes = []
         lib.repops_oracle_env_status.restype = ip
         _lib = lib
@@ -185,3 +190,35 @@ def fold_mean_sgd_f32(grads, eta, theta):
     if rc != 0:
         raise RuntimeError("oracle failed with status %d" % rc)
     return out, gbar
+
+
+def matmul_batched_f32(A: np.ndarray, B: np.ndarray, trans_a: bool = False,
+                       trans_b: bool = False, bias: np.ndarray | None = None,
+                       nthreads: int | None = None) -> np.ndarray:
+    """C_b = op(A_b) op(B_b) (+ bias_b) for stored 3-D A (batch, ., .) and B;
+    bias is (N,) (shared by all batches) or (batch, N).  Any element strides."""
+    if A.ndim != 3 or B.ndim != 3 or A.shape[0] != B.shape[0]:
+        raise ValueError("A and B must be 3-D with equal batch")
+    batch = A.shape[0]
+    M, N, K = _logical_shapes(A[0] if batch else A.reshape(A.shape[1:]),
+                              B[0] if batch else B.reshape(B.shape[1:]), trans_a, trans_b)
+    out = np.empty((batch, M, N), dtype=np.float32)
+    sa = [x // 4 for x in A.strides]
+    sb = [x // 4 for x in B.strides]
+    so = [x // 4 for x in out.strides]
+    pb, bbs, bs = None, 0, 0
+    if bias is not None:
+        bias = np.asarray(bias)
+        if bias.dtype != np.float32:
+            raise TypeError("bias must be float32")
+        if bias.ndim == 1:
+            pb, bbs, bs = bias.ctypes.data, 0, bias.strides[0] // 4
+        else:
+            pb, bbs, bs = bias.ctypes.data, bias.strides[0] // 4, bias.strides[1] // 4
+    rc = _load().repops_oracle_matmul_batched_f32(
+        A.ctypes.data, sa[0], sa[1], sa[2], B.ctypes.data, sb[0], sb[1], sb[2],
+        out.ctypes.data, so[0], so[1], so[2], M, N, K, batch, int(bool(trans_a)),
+        int(bool(trans_b)), pb, bbs, bs, nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("oracle failed with status %d" % rc)
+    return out

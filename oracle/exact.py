@@ -156,3 +156,17 @@ def exact_fold_mean_sgd(G: np.ndarray, eta, theta: np.ndarray):
         step = exact_mul(e, gb)
         out[j] = encode(exact_add(decode_binary32(int(tbits[j])), exact_neg(step)))
     return out.view(np.float32), gbar.view(np.float32)
+
+
+def exact_matmul_bias(A: np.ndarray, B: np.ndarray, bias: np.ndarray) -> np.ndarray:
+    """exact_matmul(A, B) followed by one rounded add of bias[j] per column:
+    the bias enters after the whole fixed-order sum."""
+    C = exact_matmul(A, B)
+    cbits = C.view(np.uint32)
+    bbits = np.ascontiguousarray(np.asarray(bias, dtype=np.float32)).view(np.uint32)
+    out = np.empty_like(cbits)
+    for i in range(C.shape[0]):
+        for j in range(C.shape[1]):
+            out[i, j] = encode(exact_add(decode_binary32(int(cbits[i, j])),
+                                         decode_binary32(int(bbits[j]))))
+    return out.view(np.float32)

@@ -219,3 +219,40 @@ int repops_oracle_fold_mean_sgd_f32(const float *const *grads, int64_t k, int64_
     }
     return 0;
 }
+
+/*
+ * Batched product with an optional bias, for each b in [0, batch):
+ *   C_b(i, j) = RN(S_b(i, j) + bias_b(j))   (or S_b(i, j) without a bias)
+ * where S_b(i, j) is the fixed-order sum above over op(A_b) and op(B_b), and
+ * X_b starts at X + b * x_bs.  Batch is one more free dimension (the
+ * Verde and RepOps article, section 3.2 item 1: dimensions that do not
+ * affect the order are parallelised freely).  Reading: the bias is one more
+ * separately rounded add after the whole sum (y = xW + b, with the sum
+ * complete before the bias is added); bias_b(j) = bias[b * bias_bs + j * bias_s].
+ * Returns 0, -1 for bad sizes, -2 for a bad floating-point environment.
+ */
+int repops_oracle_matmul_batched_f32(const float *A, int64_t a_bs, int64_t a_rs, int64_t a_cs,
+                                     const float *B, int64_t b_bs, int64_t b_rs, int64_t b_cs,
+                                     float *C, int64_t c_bs, int64_t c_rs, int64_t c_cs,
+                                     int64_t M, int64_t N, int64_t K, int64_t batch,
+                                     int trans_a, int trans_b,
+                                     const float *bias, int64_t bias_bs, int64_t bias_s,
+                                     int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || batch < 0) return -1;
+    if (repops_oracle_env_status() != 0) return -2;
+    for (int64_t b = 0; b < batch; ++b) {
+        float *Cb = C + b * c_bs;
+        int rc = repops_oracle_matmul_f32(A + b * a_bs, a_rs, a_cs, B + b * b_bs, b_rs, b_cs,
+                                          Cb, c_rs, c_cs, M, N, K, trans_a, trans_b, nthreads);
+        if (rc != 0) return rc;
+        if (bias) {
+            for (int64_t i = 0; i < M; ++i)
+                for (int64_t j = 0; j < N; ++j) {
+                    const float s = Cb[i * c_rs + j * c_cs];
+                    Cb[i * c_rs + j * c_cs] = s + bias[b * bias_bs + j * bias_s];
+                }
+        }
+    }
+    return 0;
+}
