@@ -31,6 +31,7 @@ from ._lib import (  # noqa: F401
     repops_canonical_order,
     repops_check_args_f32,
     repops_fold_mean_sgd_f32,
+    repops_matmul_batched_f32,
     repops_matmul_f32,
     repops_matmul_f32_ex,
     repops_pick_variant_f32,
@@ -93,6 +94,64 @@ def matmul(a, b, *, trans_a: bool = False, trans_b: bool = False, out=None, vari
                                   M, N, K, trans_a, trans_b, stream.cuda_stream, v)
     if st != REPOPS_OK:
         raise RepopsError(st, "repops_matmul_f32")
+    return out
+
+
+def _variant_index(variant):
+    if variant is None:
+        return -1
+    if isinstance(variant, str):
+        names = variant_names()
+        if variant not in names:
+            raise ValueError("unknown variant %r; known: %s" % (variant, ", ".join(names)))
+        return names.index(variant)
+    return int(variant)
+
+
+def matmul_batched(a, b, *, trans_a: bool = False, trans_b: bool = False, bias=None, out=None,
+                   variant=None, stream=None):
+    """C[n] = op(a[n]) @ op(b[n]) (+ bias) on the GPU, bit-reproducible.
+
+    ``a``/``b``: stored 3-D float32 CUDA tensors (batch, rows, cols), any
+    strides; ``bias``: (N,) shared by all batches or (batch, N), added once
+    after each fixed-order sum.  ``out``: (batch, M, N).  Returns ``out``.
+    """
+    import torch
+
+    for name, t in (("a", a), ("b", b)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 3 or t.dtype != torch.float32:
+            raise TypeError("%s must be a 3-D float32 tensor" % name)
+        if not t.is_cuda:
+            raise ValueError("%s must be on a GPU; this library has no CPU path" % name)
+    if a.shape[0] != b.shape[0]:
+        raise ValueError("batch sizes differ")
+    batch = a.shape[0]
+    M, N, K = _logical(a[0] if batch else a.new_empty(a.shape[1:]),
+                       b[0] if batch else b.new_empty(b.shape[1:]), trans_a, trans_b)
+    if out is None:
+        out = torch.empty((batch, M, N), dtype=torch.float32, device=a.device)
+    elif tuple(out.shape) != (batch, M, N) or out.dtype != torch.float32:
+        raise ValueError("out must be float32 of shape (%d, %d, %d)" % (batch, M, N))
+    bptr, bbs, bs = None, 0, 0
+    if bias is not None:
+        if bias.dtype != torch.float32 or not bias.is_cuda:
+            raise TypeError("bias must be a float32 CUDA tensor")
+        if bias.dim() == 1 and bias.shape[0] == N:
+            bptr, bbs, bs = bias.data_ptr(), 0, bias.stride(0)
+        elif bias.dim() == 2 and tuple(bias.shape) == (batch, N):
+            bptr, bbs, bs = bias.data_ptr(), bias.stride(0), bias.stride(1)
+        else:
+            raise ValueError("bias must be (N,) or (batch, N)")
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device)
+    with torch.cuda.device(a.device):
+        st = repops_matmul_batched_f32(a.data_ptr(), a.stride(0), a.stride(1), a.stride(2),
+                                       b.data_ptr(), b.stride(0), b.stride(1), b.stride(2),
+                                       out.data_ptr(), out.stride(0), out.stride(1),
+                                       out.stride(2), M, N, K, batch, trans_a, trans_b, bptr,
+                                       bbs, bs, stream.cuda_stream, _variant_index(variant))
+    if st != REPOPS_OK:
+        raise RepopsError(st, "repops_matmul_batched_f32")
     return out
 
 

@@ -25,6 +25,7 @@ REPOPS_FOLD_MAX_PER_PASS = 64
 EXPORTS = (
     "repops_matmul_f32",
     "repops_matmul_f32_ex",
+    "repops_matmul_batched_f32",
     "repops_check_args_f32",
     "repops_pick_variant_f32",
     "repops_variant_count",
@@ -60,6 +61,10 @@ def load():
     lib.repops_matmul_f32.restype = ci
     lib.repops_matmul_f32_ex.argtypes = mm + [vp, ci]
     lib.repops_matmul_f32_ex.restype = ci
+    lib.repops_matmul_batched_f32.argtypes = [vp, i64, i64, i64, vp, i64, i64, i64, vp, i64, i64,
+                                              i64, i64, i64, i64, i64, ci, ci, vp, i64, i64,
+                                              vp, ci]
+    lib.repops_matmul_batched_f32.restype = ci
     lib.repops_check_args_f32.argtypes = mm + [ci]
     lib.repops_check_args_f32.restype = ci
     lib.repops_pick_variant_f32.argtypes = [vp, i64, i64, vp, i64, i64, i64, i64, i64, ci, ci]
@@ -91,6 +96,15 @@ def repops_matmul_f32_ex(A, a_rs, a_cs, B, b_rs, b_cs, C, c_rs, c_cs, M, N, K, t
                          stream, variant) -> int:
     return load().repops_matmul_f32_ex(A, a_rs, a_cs, B, b_rs, b_cs, C, c_rs, c_cs, M, N, K,
                                        int(trans_a), int(trans_b), stream, int(variant))
+
+
+def repops_matmul_batched_f32(A, a_bs, a_rs, a_cs, B, b_bs, b_rs, b_cs, C, c_bs, c_rs, c_cs, M,
+                              N, K, batch, trans_a, trans_b, bias, bias_bs, bias_s, stream,
+                              variant=-1) -> int:
+    return load().repops_matmul_batched_f32(A, a_bs, a_rs, a_cs, B, b_bs, b_rs, b_cs, C, c_bs,
+                                            c_rs, c_cs, M, N, K, batch, int(trans_a),
+                                            int(trans_b), bias, bias_bs, bias_s, stream,
+                                            int(variant))
 
 
 def repops_check_args_f32(A, a_rs, a_cs, B, b_rs, b_cs, C, c_rs, c_cs, M, N, K, trans_a, trans_b,

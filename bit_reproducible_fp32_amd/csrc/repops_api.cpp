@@ -67,18 +67,20 @@ constexpr int64_t kMaxBlocks = (int64_t(1) << 32) / 256 - 1;
 struct Problem {
     OperandView a, b;
     OutView c;
-    int64_t M, N, K;
+    int64_t M, N, K, batch;
 };
 
-// Largest element offset reached by (rows x cols) with strides (rs, cs), or
-// -1 on int64 overflow.  Requires rows, cols >= 1 and rs, cs >= 0.
-int64_t max_offset(int64_t rows, int64_t cols, int64_t rs, int64_t cs) {
-    int64_t a, b, s;
-    if (__builtin_mul_overflow(rows - 1, rs, &a)) return -1;
-    if (__builtin_mul_overflow(cols - 1, cs, &b)) return -1;
-    if (__builtin_add_overflow(a, b, &s)) return -1;
-    if (s > INT64_MAX / 4 - 4) return -1;  // byte offsets must fit too
-    return s;
+// Largest element offset reached by a (d0 x d1 x d2) block with strides
+// (s0, s1, s2), or -1 on int64 overflow.  Requires d >= 1, s >= 0.
+int64_t max_offset3(int64_t d0, int64_t d1, int64_t d2, int64_t s0, int64_t s1, int64_t s2) {
+    int64_t a, b, c, t, u;
+    if (__builtin_mul_overflow(d0 - 1, s0, &a)) return -1;
+    if (__builtin_mul_overflow(d1 - 1, s1, &b)) return -1;
+    if (__builtin_mul_overflow(d2 - 1, s2, &c)) return -1;
+    if (__builtin_add_overflow(a, b, &t)) return -1;
+    if (__builtin_add_overflow(t, c, &u)) return -1;
+    if (u > INT64_MAX / 4 - 4) return -1;  // byte offsets must fit too
+    return u;
 }
 
 bool overlaps(const void* p, int64_t p_elems, const void* q, int64_t q_elems) {
@@ -88,26 +90,29 @@ bool overlaps(const void* p, int64_t p_elems, const void* q, int64_t q_elems) {
     return p0 < q1 && q0 < p1;
 }
 
-// C's strides map distinct (i, j) to distinct elements.  Sufficient test
-// (strides >= 0): the smaller stride is nonzero when its extent is > 1 and
-// the larger stride steps over a whole run of the smaller one.
-bool injective(int64_t M, int64_t N, int64_t s_i, int64_t s_j) {
-    if (M > 1 && s_i == 0) return false;
-    if (N > 1 && s_j == 0) return false;
-    if (M <= 1 || N <= 1) return true;
-    int64_t s_small = s_i, d_small = M, s_big = s_j;
-    if (s_j < s_i || (s_j == s_i && N < M)) {
-        s_small = s_j; d_small = N; s_big = s_i;
+// The map (b, i, j) -> b*s0 + i*s1 + j*s2 is injective on the index box.
+// Sufficient test (strides >= 0): ordering the axes with extent > 1 by
+// stride, each stride exceeds the largest offset the smaller ones reach.
+bool injective3(int64_t d0, int64_t d1, int64_t d2, int64_t s0, int64_t s1, int64_t s2) {
+    struct Axis {
+        int64_t s, d;
+    } ax[3] = {{s0, d0}, {s1, d1}, {s2, d2}};
+    std::sort(ax, ax + 3, [](const Axis& x, const Axis& y) { return x.s < y.s; });
+    int64_t reach = 0;  // largest offset reached by the axes so far
+    for (const Axis& a : ax) {
+        if (a.d <= 1) continue;
+        if (a.s <= reach) return false;
+        int64_t span;
+        if (__builtin_mul_overflow(a.s, a.d - 1, &span)) return false;
+        if (__builtin_add_overflow(reach, span, &reach)) return false;
     }
-    int64_t need;
-    if (__builtin_mul_overflow(s_small, d_small, &need)) return false;
-    return s_big >= need;
+    return true;
 }
 
 // Sizes, flags and variant index.
-repops_status check_dims(int64_t M, int64_t N, int64_t K, int trans_a, int trans_b,
-                         int variant) {
-    if (M < 0 || N < 0 || K < 0) return REPOPS_ERR_DIM;
+repops_status check_dims(int64_t M, int64_t N, int64_t K, int64_t batch, int trans_a,
+                         int trans_b, int variant) {
+    if (M < 0 || N < 0 || K < 0 || batch < 0) return REPOPS_ERR_DIM;
     if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1)) return REPOPS_ERR_DIM;
     if (variant < -1 || variant >= kNumVariants) return REPOPS_ERR_VARIANT;
     // Grid limits: the largest grid any variant launches for these sizes.
@@ -119,49 +124,60 @@ repops_status check_dims(int64_t M, int64_t N, int64_t K, int trans_a, int trans
 
 // A and B (only when K > 0): pointers, strides, offset overflow; fills the
 // X x K operand views and their element extents.
-repops_status check_operands(const float* A, int64_t a_rs, int64_t a_cs, const float* B,
-                             int64_t b_rs, int64_t b_cs, int64_t M, int64_t N, int64_t K,
-                             int trans_a, int trans_b, Problem* p, int64_t* a_extent,
-                             int64_t* b_extent) {
+repops_status check_operands(const float* A, int64_t a_bs, int64_t a_rs, int64_t a_cs,
+                             const float* B, int64_t b_bs, int64_t b_rs, int64_t b_cs, int64_t M,
+                             int64_t N, int64_t K, int64_t batch, int trans_a, int trans_b,
+                             Problem* p, int64_t* a_extent, int64_t* b_extent) {
     if (A == nullptr || B == nullptr) return REPOPS_ERR_NULL;
-    if (a_rs < 0 || a_cs < 0 || b_rs < 0 || b_cs < 0) return REPOPS_ERR_STRIDE;
+    if (a_bs < 0 || a_rs < 0 || a_cs < 0 || b_bs < 0 || b_rs < 0 || b_cs < 0)
+        return REPOPS_ERR_STRIDE;
     // Stored shapes: A is M x K (K x M when transposed), B is K x N (N x K).
     const int64_t a_rows = trans_a ? K : M, a_cols = trans_a ? M : K;
     const int64_t b_rows = trans_b ? N : K, b_cols = trans_b ? K : N;
-    const int64_t a_max = max_offset(a_rows, a_cols, a_rs, a_cs);
-    const int64_t b_max = max_offset(b_rows, b_cols, b_rs, b_cs);
+    const int64_t a_max = max_offset3(batch, a_rows, a_cols, a_bs, a_rs, a_cs);
+    const int64_t b_max = max_offset3(batch, b_rows, b_cols, b_bs, b_rs, b_cs);
     if (a_max < 0 || b_max < 0) return REPOPS_ERR_DIM;
     // op(A)(i, k) and op(B)(k, j) as X x K views.
-    p->a = OperandView{A, trans_a ? a_cs : a_rs, trans_a ? a_rs : a_cs, M};
-    p->b = OperandView{B, trans_b ? b_rs : b_cs, trans_b ? b_cs : b_rs, N};
+    p->a = OperandView{A, trans_a ? a_cs : a_rs, trans_a ? a_rs : a_cs, M, a_bs};
+    p->b = OperandView{B, trans_b ? b_rs : b_cs, trans_b ? b_cs : b_rs, N, b_bs};
     *a_extent = a_max + 1;
     *b_extent = b_max + 1;
     return REPOPS_OK;
 }
 
-repops_status validate(const float* A, int64_t a_rs, int64_t a_cs, const float* B, int64_t b_rs,
-                       int64_t b_cs, const float* C, int64_t c_rs, int64_t c_cs, int64_t M,
-                       int64_t N, int64_t K, int trans_a, int trans_b, int variant,
-                       Problem* out) {
-    repops_status st = check_dims(M, N, K, trans_a, trans_b, variant);
+repops_status validate(const float* A, int64_t a_bs, int64_t a_rs, int64_t a_cs, const float* B,
+                       int64_t b_bs, int64_t b_rs, int64_t b_cs, const float* C, int64_t c_bs,
+                       int64_t c_rs, int64_t c_cs, int64_t M, int64_t N, int64_t K,
+                       int64_t batch, int trans_a, int trans_b, const float* bias,
+                       int64_t bias_bs, int64_t bias_s, int variant, Problem* out) {
+    repops_status st = check_dims(M, N, K, batch, trans_a, trans_b, variant);
     if (st != REPOPS_OK) return st;
-    if (M == 0 || N == 0) return REPOPS_OK;  // nothing to do
+    if (M == 0 || N == 0 || batch == 0) return REPOPS_OK;  // nothing to do
     if (C == nullptr) return REPOPS_ERR_NULL;
     Problem p{};
-    p.M = M; p.N = N; p.K = K;
+    p.M = M; p.N = N; p.K = K; p.batch = batch;
     int64_t a_extent = 0, b_extent = 0;
     if (K > 0) {
-        st = check_operands(A, a_rs, a_cs, B, b_rs, b_cs, M, N, K, trans_a, trans_b, &p,
-                            &a_extent, &b_extent);
+        st = check_operands(A, a_bs, a_rs, a_cs, B, b_bs, b_rs, b_cs, M, N, K, batch, trans_a,
+                            trans_b, &p, &a_extent, &b_extent);
         if (st != REPOPS_OK) return st;
     }
-    if (c_rs < 0 || c_cs < 0) return REPOPS_ERR_STRIDE;
-    const int64_t c_max = max_offset(M, N, c_rs, c_cs);
+    if (c_bs < 0 || c_rs < 0 || c_cs < 0) return REPOPS_ERR_STRIDE;
+    const int64_t c_max = max_offset3(batch, M, N, c_bs, c_rs, c_cs);
     if (c_max < 0) return REPOPS_ERR_DIM;
-    if (!injective(M, N, c_rs, c_cs)) return REPOPS_ERR_STRIDE;
+    if (!injective3(batch, M, N, c_bs, c_rs, c_cs)) return REPOPS_ERR_STRIDE;
     if (K > 0 && (overlaps(C, c_max + 1, A, a_extent) || overlaps(C, c_max + 1, B, b_extent)))
         return REPOPS_ERR_ALIAS;
-    p.c = OutView{const_cast<float*>(C), c_rs, c_cs};
+    p.c = OutView{const_cast<float*>(C), c_rs, c_cs, c_bs, nullptr, 0, 0};
+    if (bias != nullptr) {
+        if (bias_bs < 0 || bias_s < 0) return REPOPS_ERR_STRIDE;
+        const int64_t bias_max = max_offset3(batch, 1, N, bias_bs, 0, bias_s);
+        if (bias_max < 0) return REPOPS_ERR_DIM;
+        if (overlaps(C, c_max + 1, bias, bias_max + 1)) return REPOPS_ERR_ALIAS;
+        p.c.bias = bias;
+        p.c.bias_s = bias_s;
+        p.c.bias_sb = bias_bs;
+    }
     if (out) *out = p;
     return REPOPS_OK;
 }
@@ -171,8 +187,9 @@ bool aligned16(const float* p) { return (reinterpret_cast<uintptr_t>(p) & 15) ==
 // Fast loaders need unit stride along one axis, 16-byte aligned base and a
 // multiple-of-4 stride along the other axis (so every float4 is aligned);
 // loads along x also need 4 | X so a clamped vector stays inside the operand.
-int classify(const OperandView& v, int64_t K) {
+int classify(const OperandView& v, int64_t K, int64_t batch) {
     if (!aligned16(v.p)) return LAY_GEN;
+    if (batch > 1 && v.s_b % 4 != 0) return LAY_GEN;  // every batch's base must stay aligned
     if (v.s_k == 1 && (v.s_x % 4 == 0 || v.X == 1)) return LAY_KC;
     if (v.s_x == 1 && (v.s_k % 4 == 0 || K == 1) && v.X % 4 == 0) return LAY_XC;
     return LAY_GEN;
@@ -181,7 +198,7 @@ int classify(const OperandView& v, int64_t K) {
 int pick(const Problem& p) {
     static const int large = variant_index("mprod1_t128x128x16_w8_xcd");
     static const int small = variant_index("valu_t64x64x16_r4x4_row");
-    const int64_t tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128);
+    const int64_t tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch;
     // 256 CUs: 128x128 product tiles when there are at least two per CU;
     // below that the problem cannot fill the chip and the 64x64 VALU tiles
     // (more workgroups, measured faster at 256^3 and 1024^3) win.
@@ -189,39 +206,61 @@ int pick(const Problem& p) {
 }
 
 repops_status run(const Problem& p, int variant, void* stream) {
-    if (p.M == 0 || p.N == 0) return REPOPS_OK;
-    int err;
-    if (p.K == 0) {
-        err = launch_fill_zero(p.c, p.M, p.N, stream);
-    } else {
-        const int v = variant < 0 ? pick(p) : variant;
-        const Variant& var = kVariants[v];
-        if (var.kind == KIND_NAIVE) {
-            err = launch_naive(p.a, p.b, p.c, p.M, p.N, p.K, stream);
-        } else if (var.kind == KIND_MPROD) {
-            err = launch_mprod(var.cfg, classify(p.a, p.K), classify(p.b, p.K), p.a, p.b, p.c,
-                               p.M, p.N, p.K, var.order, stream);
+    if (p.M == 0 || p.N == 0 || p.batch == 0) return REPOPS_OK;
+    const int v = p.K == 0 ? -1 : (variant < 0 ? pick(p) : variant);
+    const int la = p.K == 0 ? 0 : classify(p.a, p.K, p.batch);
+    const int lb = p.K == 0 ? 0 : classify(p.b, p.K, p.batch);
+    // The grid's batch dimension is limited; longer batches run in chunks.
+    for (int64_t b0 = 0; b0 < p.batch; b0 += kMaxBatchPerLaunch) {
+        const int64_t nb = p.batch - b0 < kMaxBatchPerLaunch ? p.batch - b0 : kMaxBatchPerLaunch;
+        OperandView a = p.a, b = p.b;
+        OutView c = p.c;
+        a.p += b0 * a.s_b;
+        b.p += b0 * b.s_b;
+        c.p += b0 * c.s_b;
+        if (c.bias) c.bias += b0 * c.bias_sb;
+        int err;
+        if (p.K == 0) {
+            err = launch_fill_zero(c, p.M, p.N, nb, stream);
+        } else if (kVariants[v].kind == KIND_NAIVE) {
+            err = launch_naive(a, b, c, p.M, p.N, p.K, nb, stream);
+        } else if (kVariants[v].kind == KIND_MPROD) {
+            err = launch_mprod(kVariants[v].cfg, la, lb, a, b, c, p.M, p.N, p.K, nb,
+                               kVariants[v].order, stream);
         } else {
-            err = launch_tiled(var.cfg, classify(p.a, p.K), classify(p.b, p.K), p.a, p.b, p.c,
-                               p.M, p.N, p.K, var.order, stream);
+            err = launch_tiled(kVariants[v].cfg, la, lb, a, b, c, p.M, p.N, p.K, nb,
+                               kVariants[v].order, stream);
         }
+        if (err != 0) return REPOPS_ERR_HIP;
     }
-    return err == 0 ? REPOPS_OK : REPOPS_ERR_HIP;
+    return REPOPS_OK;
 }
 
 }  // namespace
 
 extern "C" {
 
+repops_status repops_matmul_batched_f32(const float* A, int64_t a_bs, int64_t a_rs, int64_t a_cs,
+                                        const float* B, int64_t b_bs, int64_t b_rs, int64_t b_cs,
+                                        float* C, int64_t c_bs, int64_t c_rs, int64_t c_cs,
+                                        int64_t M, int64_t N, int64_t K, int64_t batch,
+                                        int trans_a, int trans_b, const float* bias,
+                                        int64_t bias_bs, int64_t bias_s, void* stream,
+                                        int variant) {
+    Problem p{};
+    const repops_status st = validate(A, a_bs, a_rs, a_cs, B, b_bs, b_rs, b_cs, C, c_bs, c_rs,
+                                      c_cs, M, N, K, batch, trans_a, trans_b, bias, bias_bs,
+                                      bias_s, variant, &p);
+    if (st != REPOPS_OK) return st;
+    return run(p, variant, stream);
+}
+
 repops_status repops_matmul_f32_ex(const float* A, int64_t a_rs, int64_t a_cs, const float* B,
                                    int64_t b_rs, int64_t b_cs, float* C, int64_t c_rs,
                                    int64_t c_cs, int64_t M, int64_t N, int64_t K, int trans_a,
                                    int trans_b, void* stream, int variant) {
-    Problem p{};
-    const repops_status st = validate(A, a_rs, a_cs, B, b_rs, b_cs, C, c_rs, c_cs, M, N, K,
-                                      trans_a, trans_b, variant, &p);
-    if (st != REPOPS_OK) return st;
-    return run(p, variant, stream);
+    return repops_matmul_batched_f32(A, 0, a_rs, a_cs, B, 0, b_rs, b_cs, C, 0, c_rs, c_cs, M, N,
+                                     K, 1, trans_a, trans_b, nullptr, 0, 0, stream, variant);
 }
 
 repops_status repops_matmul_f32(const float* A, int64_t a_rs, int64_t a_cs, const float* B,
@@ -236,20 +275,20 @@ repops_status repops_check_args_f32(const float* A, int64_t a_rs, int64_t a_cs, 
                                     int64_t b_rs, int64_t b_cs, const float* C, int64_t c_rs,
                                     int64_t c_cs, int64_t M, int64_t N, int64_t K, int trans_a,
                                     int trans_b, int variant) {
-    return validate(A, a_rs, a_cs, B, b_rs, b_cs, C, c_rs, c_cs, M, N, K, trans_a, trans_b,
-                    variant, nullptr);
+    return validate(A, 0, a_rs, a_cs, B, 0, b_rs, b_cs, C, 0, c_rs, c_cs, M, N, K, 1, trans_a,
+                    trans_b, nullptr, 0, 0, variant, nullptr);
 }
 
 int repops_pick_variant_f32(const float* A, int64_t a_rs, int64_t a_cs, const float* B,
                             int64_t b_rs, int64_t b_cs, int64_t M, int64_t N, int64_t K,
                             int trans_a, int trans_b) {
     if (M <= 0 || N <= 0 || K <= 0) return -1;
-    if (check_dims(M, N, K, trans_a, trans_b, -1) != REPOPS_OK) return -1;
+    if (check_dims(M, N, K, 1, trans_a, trans_b, -1) != REPOPS_OK) return -1;
     Problem p{};
-    p.M = M; p.N = N; p.K = K;
+    p.M = M; p.N = N; p.K = K; p.batch = 1;
     int64_t ae, be;
-    if (check_operands(A, a_rs, a_cs, B, b_rs, b_cs, M, N, K, trans_a, trans_b, &p, &ae, &be) !=
-        REPOPS_OK)
+    if (check_operands(A, 0, a_rs, a_cs, B, 0, b_rs, b_cs, M, N, K, 1, trans_a, trans_b, &p, &ae,
+                       &be) != REPOPS_OK)
         return -1;
     return pick(p);
 }

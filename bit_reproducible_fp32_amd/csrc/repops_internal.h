@@ -6,21 +6,28 @@
 
 namespace repops {
 
-// One operand seen as an X x K matrix: element (x, k) is p[x*s_x + k*s_k].
-// For A, x is the output row i; for B, x is the output column j.  Both
-// operands therefore share one loader and one LDS layout.
+// One operand seen as an X x K matrix: element (x, k) of batch b is
+// p[b*s_b + x*s_x + k*s_k].  For A, x is the output row i; for B, x is the
+// output column j.  Both operands therefore share one loader and one LDS
+// layout.
 struct OperandView {
     const float* p;
     int64_t s_x;
     int64_t s_k;
     int64_t X;
+    int64_t s_b;
 };
 
-// Output: element (i, j) is p[i*s_i + j*s_j].
+// Output: element (i, j) of batch b is p[b*s_b + i*s_i + j*s_j].  With a
+// bias, the stored value is RN(sum + bias[b*bias_sb + j*bias_s]).
 struct OutView {
     float* p;
     int64_t s_i;
     int64_t s_j;
+    int64_t s_b;
+    const float* bias;  // nullptr: no bias
+    int64_t bias_s;
+    int64_t bias_sb;
 };
 
 // How an operand tile is fetched from global memory.
@@ -77,14 +84,17 @@ FastDiv make_fastdiv(uint32_t d);
 TileGrid make_tile_grid(int tiles_m, int tiles_n, int order);
 void tile_shape(int cfg, int* bm, int* bn);
 
-// Each returns a hipError_t value (0 on success) from the launch.
+// Each returns a hipError_t value (0 on success) from the launch.  `batch`
+// (1..kMaxBatchPerLaunch) is the grid's second dimension; each batch index
+// offsets A, B, C and the bias by their batch strides.
+constexpr int64_t kMaxBatchPerLaunch = 65535;
 int launch_tiled(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, OutView C,
-                 int64_t M, int64_t N, int64_t K, int order, void* stream);
+                 int64_t M, int64_t N, int64_t K, int64_t batch, int order, void* stream);
 int launch_mprod(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, OutView C,
-                 int64_t M, int64_t N, int64_t K, int order, void* stream);
+                 int64_t M, int64_t N, int64_t K, int64_t batch, int order, void* stream);
 int launch_naive(OperandView A, OperandView B, OutView C, int64_t M, int64_t N, int64_t K,
-                 void* stream);
-int launch_fill_zero(OutView C, int64_t M, int64_t N, void* stream);
+                 int64_t batch, void* stream);
+int launch_fill_zero(OutView C, int64_t M, int64_t N, int64_t batch, void* stream);
 
 // Fixed-order gradient fold: the contributors one pass reads, in fold order.
 constexpr int kFoldMax = 64;

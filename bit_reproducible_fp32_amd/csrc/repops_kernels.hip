@@ -31,6 +31,21 @@ constexpr int kPad = 4;  // LDS row padding (floats); keeps rows 16-byte aligned
 __device__ __forceinline__ float mul_rn(float a, float b) { return a * b; }
 __device__ __forceinline__ float add_rn(float a, float b) { return a + b; }
 
+// Moves the views to batch blockIdx.y (batch is a free dimension).
+__device__ __forceinline__ void select_batch(OperandView& A, OperandView& B, OutView& C) {
+    const int64_t b = blockIdx.y;
+    A.p += b * A.s_b;
+    B.p += b * B.s_b;
+    C.p += b * C.s_b;
+    if (C.bias) C.bias += b * C.bias_sb;
+}
+
+// The stored value of output column j: the fixed-order sum, then (with a
+// bias) one more separately rounded add.
+__device__ __forceinline__ float epilogue_value(const OutView& C, int64_t j, float sum) {
+    return C.bias ? add_rn(sum, C.bias[j * C.bias_s]) : sum;
+}
+
 // ---------------------------------------------------------------------------
 // Global -> register -> LDS staging of one X x BK operand tile.
 // LDS holds the tile k-major: lds[k * (BX + kPad) + x].  Each lane owns kNV
@@ -255,6 +270,7 @@ __global__ __launch_bounds__(kThreads) void repops_tiled_kernel(OperandView A, O
     const int ty = tid / (BN / TN);
     int tm, tn;
     tile_of_block(grid, tm, tn);
+    select_batch(A, B, C);
     const int64_t m0 = static_cast<int64_t>(tm) * BM;
     const int64_t n0 = static_cast<int64_t>(tn) * BN;
 
@@ -325,11 +341,14 @@ __global__ __launch_bounds__(kThreads) void repops_tiled_kernel(OperandView A, O
                 const int64_t j0 = n0 + h * CSPAN + tx * 4;
                 const float* v = &acc[4 * g + e][4 * h];
                 if (vec_store && j0 + 3 < N) {
-                    *reinterpret_cast<float4*>(C.p + i * C.s_i + j0) = make_float4(v[0], v[1], v[2], v[3]);
+                    *reinterpret_cast<float4*>(C.p + i * C.s_i + j0) =
+                        make_float4(epilogue_value(C, j0, v[0]), epilogue_value(C, j0 + 1, v[1]),
+                                    epilogue_value(C, j0 + 2, v[2]), epilogue_value(C, j0 + 3, v[3]));
                 } else {
 #pragma unroll
                     for (int f = 0; f < 4; ++f)
-                        if (j0 + f < N) C.p[i * C.s_i + (j0 + f) * C.s_j] = v[f];
+                        if (j0 + f < N)
+                            C.p[i * C.s_i + (j0 + f) * C.s_j] = epilogue_value(C, j0 + f, v[f]);
                 }
             }
         }
@@ -510,6 +529,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void repops_mprod16_kernel(
     const int wm = wave % WAVES_M, wn = wave / WAVES_M;
     int tm, tn;
     tile_of_block(grid, tm, tn);
+    select_batch(A, B, C);
     const int64_t m0 = static_cast<int64_t>(tm) * BM;
     const int64_t n0 = static_cast<int64_t>(tn) * BN;
 
@@ -571,7 +591,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void repops_mprod16_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int64_t i = m0 + wm * 64 + mprod16_row(v, lane);
-            if (i < M) C.p[i * C.s_i + j * C.s_j] = acc[t][v];
+            if (i < M) C.p[i * C.s_i + j * C.s_j] = epilogue_value(C, j, acc[t][v]);
         }
     }
 }
@@ -592,6 +612,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void repops_mprod_kernel(
     const int wm = wave % WAVES_M, wn = wave / WAVES_M;
     int tm, tn;
     tile_of_block(grid, tm, tn);
+    select_batch(A, B, C);
     const int64_t m0 = static_cast<int64_t>(tm) * BM;
     const int64_t n0 = static_cast<int64_t>(tn) * BN;
 
@@ -655,7 +676,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void repops_mprod_kernel(
 #pragma unroll
         for (int v = 0; v < 32; ++v) {
             const int64_t i = m0 + wm * 64 + mprod_row(v, lane);
-            if (i < M) C.p[i * C.s_i + j * C.s_j] = acc[t][v];
+            if (i < M) C.p[i * C.s_i + j * C.s_j] = epilogue_value(C, j, acc[t][v]);
         }
     }
 }
@@ -671,18 +692,23 @@ __global__ __launch_bounds__(256) void repops_naive_kernel(OperandView A, Operan
     const int64_t i = static_cast<int64_t>(by) * 16 + threadIdx.x / 16;
     const int64_t j = static_cast<int64_t>(bx) * 16 + threadIdx.x % 16;
     if (i >= M || j >= N) return;
+    select_batch(A, B, C);
     const float* a = A.p + i * A.s_x;
     const float* b = B.p + j * B.s_x;
     float s = 0.0f;
     for (int64_t k = 0; k < K; ++k) s = add_rn(s, mul_rn(a[k * A.s_k], b[k * B.s_k]));
-    C.p[i * C.s_i + j * C.s_j] = s;
+    C.p[i * C.s_i + j * C.s_j] = epilogue_value(C, j, s);
 }
 
-// K == 0: every output is the empty sum, +0.  Grid-stride over rows and
-// columns (no integer division).
+// K == 0: every sum is empty, +0 (then the bias, if any, is added to it).
+// Grid-stride over rows and columns (no integer division).
 __global__ __launch_bounds__(256) void repops_fill_zero_kernel(OutView C, int64_t M, int64_t N) {
+    const int64_t b = blockIdx.y;
+    C.p += b * C.s_b;
+    if (C.bias) C.bias += b * C.bias_sb;
     for (int64_t i = blockIdx.x; i < M; i += gridDim.x)
-        for (int64_t j = threadIdx.x; j < N; j += 256) C.p[i * C.s_i + j * C.s_j] = 0.0f;
+        for (int64_t j = threadIdx.x; j < N; j += 256)
+            C.p[i * C.s_i + j * C.s_j] = epilogue_value(C, j, 0.0f);
 }
 
 // ---------------------------------------------------------------------------
@@ -776,12 +802,13 @@ void tile_shape(int cfg, int* bm, int* bn) {
 }
 
 int launch_mprod(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, OutView C,
-                 int64_t M, int64_t N, int64_t K, int order, void* stream) {
+                 int64_t M, int64_t N, int64_t K, int64_t batch, int order, void* stream) {
     int bm, bn;
     tile_shape(cfg, &bm, &bn);
     const int tiles_m = static_cast<int>((M + bm - 1) / bm);
     const int tiles_n = static_cast<int>((N + bn - 1) / bn);
-    const dim3 grid(static_cast<unsigned>(tiles_m) * static_cast<unsigned>(tiles_n));
+    const dim3 grid(static_cast<unsigned>(tiles_m) * static_cast<unsigned>(tiles_n),
+                    static_cast<unsigned>(batch));
     hipStream_t s = static_cast<hipStream_t>(stream);
     TiledFn fn;
     int threads;
@@ -803,12 +830,13 @@ int launch_mprod(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, Ou
 }
 
 int launch_tiled(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, OutView C,
-                 int64_t M, int64_t N, int64_t K, int order, void* stream) {
+                 int64_t M, int64_t N, int64_t K, int64_t batch, int order, void* stream) {
     int bm, bn;
     tile_shape(cfg, &bm, &bn);
     const int tiles_m = static_cast<int>((M + bm - 1) / bm);
     const int tiles_n = static_cast<int>((N + bn - 1) / bn);
-    const dim3 grid(static_cast<unsigned>(tiles_m) * static_cast<unsigned>(tiles_n));
+    const dim3 grid(static_cast<unsigned>(tiles_m) * static_cast<unsigned>(tiles_n),
+                    static_cast<unsigned>(batch));
     const dim3 block(kThreads);
     hipStream_t s = static_cast<hipStream_t>(stream);
     TiledFn fn;
@@ -824,19 +852,20 @@ int launch_tiled(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, Ou
 }
 
 int launch_naive(OperandView A, OperandView B, OutView C, int64_t M, int64_t N, int64_t K,
-                 void* stream) {
+                 int64_t batch, void* stream) {
     const int blocks_n = static_cast<int>((N + 15) / 16);
     const int blocks_m = static_cast<int>((M + 15) / 16);
     hipLaunchKernelGGL(repops_naive_kernel,
-                       dim3(static_cast<unsigned>(blocks_m) * static_cast<unsigned>(blocks_n)),
+                       dim3(static_cast<unsigned>(blocks_m) * static_cast<unsigned>(blocks_n),
+                            static_cast<unsigned>(batch)),
                        dim3(256), 0, static_cast<hipStream_t>(stream), A, B, C, M, N, K,
                        make_fastdiv(static_cast<uint32_t>(blocks_n)));
     return static_cast<int>(hipGetLastError());
 }
 
-int launch_fill_zero(OutView C, int64_t M, int64_t N, void* stream) {
+int launch_fill_zero(OutView C, int64_t M, int64_t N, int64_t batch, void* stream) {
     const unsigned blocks = static_cast<unsigned>(M < 65536 ? M : 65536);
-    hipLaunchKernelGGL(repops_fill_zero_kernel, dim3(blocks), dim3(256), 0,
+    hipLaunchKernelGGL(repops_fill_zero_kernel, dim3(blocks, static_cast<unsigned>(batch)), dim3(256), 0,
                        static_cast<hipStream_t>(stream), C, M, N);
     return static_cast<int>(hipGetLastError());
 }

@@ -176,3 +176,45 @@ def fold_sample_indices(d: int, count: int, seed: int):
     idx = list(range(min(d, 64))) + list(range(max(0, d - 64), d))
     idx += list(rng.integers(0, d, size=count))
     return np.unique(np.asarray(idx, dtype=np.int64))
+
+
+@dataclass(frozen=True)
+class BatchedWorkload:
+    """A batch of independent fixed-order products (batch is a free
+    dimension), as in multi-head attention."""
+    name: str
+    batch: int
+    M: int
+    N: int
+    K: int
+    trans_a: bool
+    trans_b: bool
+    a_dist: str
+    b_dist: str
+    seed: int
+    description: str
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.batch * self.M * self.N * self.K
+
+
+BATCHED_WORKLOADS = {
+    w.name: w
+    for w in [
+        BatchedWorkload("llama8b_attn_scores", 32, 2048, 2048, 128, False, True, "normal1",
+                        "normal1", 7001, "Llama-3.1-8B-shaped attention scores Q K^T: 32 "
+                        "heads, S=2048, head dim 128; Q and K stored (32, 2048, 128)"),
+        BatchedWorkload("llama8b_attn_pv", 32, 2048, 128, 2048, False, False, "normal0.02",
+                        "normal1", 7101, "Llama-3.1-8B-shaped P V: 32 heads, P (2048 x 2048), "
+                        "V (2048 x 128)"),
+    ]
+}
+
+
+def make_batched_operands(name: str):
+    """(A, B) as stored 3-D float32 arrays for a batched workload."""
+    w = BATCHED_WORKLOADS[name]
+    a_shape = (w.batch, w.K, w.M) if w.trans_a else (w.batch, w.M, w.K)
+    b_shape = (w.batch, w.N, w.K) if w.trans_b else (w.batch, w.K, w.N)
+    return _draw(w.a_dist, a_shape, w.seed + 1), _draw(w.b_dist, b_shape, w.seed + 2)

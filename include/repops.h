@@ -90,6 +90,30 @@ repops_status repops_matmul_f32_ex(const float* A, int64_t a_rs, int64_t a_cs,
                                    int variant);
 
 /*
+ * Batched form with an optional bias epilogue.  For each b in [0, batch),
+ * with X_b = X + b * x_bs for each of A, B and C (strides in elements):
+ *
+ *     C_b(i, j) = RN(S_b(i, j) + bias[b*bias_bs + j*bias_s])   (bias != NULL)
+ *     C_b(i, j) = S_b(i, j)                                     (bias == NULL)
+ *
+ * where S_b is the fixed-order sum of op(A_b) op(B_b) defined above.  Batch
+ * is one more free dimension (the Verde and RepOps article, section 3.2
+ * item 1: dimensions that do not touch the order are parallelised freely);
+ * the bias is one more separately rounded add after the whole sum (a bias of
+ * -0 on an exact-zero sum gives +0).  K == 0 gives RN(+0 + bias).
+ * `variant` as in repops_matmul_f32_ex (-1: automatic).  Batch strides must
+ * be >= 0; C's (b, i, j) must map to distinct elements; C may not overlap A,
+ * B or the bias.  batch == 0 is a successful no-op.  Errors as above.
+ */
+repops_status repops_matmul_batched_f32(const float* A, int64_t a_bs, int64_t a_rs, int64_t a_cs,
+                                        const float* B, int64_t b_bs, int64_t b_rs, int64_t b_cs,
+                                        float* C, int64_t c_bs, int64_t c_rs, int64_t c_cs,
+                                        int64_t M, int64_t N, int64_t K, int64_t batch,
+                                        int trans_a, int trans_b,
+                                        const float* bias, int64_t bias_bs, int64_t bias_s,
+                                        void* stream, int variant);
+
+/*
  * Validates the arguments exactly as repops_matmul_f32_ex does and returns
  * the status that call would return before queueing anything.  Queues
  * nothing and touches no device: A, B and C are compared as addresses and

@@ -235,3 +235,40 @@ def test_assembly_matches_the_library_build():
     """The scanned assembly is at least as new as the kernel source."""
     src = os.path.join(ROOT, "bit_reproducible_fp32_amd", "csrc", "repops_kernels.hip")
     assert os.path.getmtime(ASM) >= os.path.getmtime(src) - 1
+
+
+def bok(**kw):
+    """repops_matmul_batched_f32 through calls that all fail validation, so
+    nothing is ever launched."""
+    args = dict(A=PA, a_bs=16 * 64, a_rs=64, a_cs=1, B=PB, b_bs=64 * 32, b_rs=32, b_cs=1,
+                C=PC, c_bs=16 * 32, c_rs=32, c_cs=1, M=16, N=32, K=64, batch=3,
+                trans_a=0, trans_b=0, bias=None, bias_bs=0, bias_s=1, stream=0, variant=-1)
+    args.update(kw)
+    return rp.repops_matmul_batched_f32(**args)
+
+
+def test_batched_validation_errors():
+    assert bok(batch=-1) == rp.REPOPS_ERR_DIM
+    assert bok(a_bs=-1) == rp.REPOPS_ERR_STRIDE
+    assert bok(c_bs=-32) == rp.REPOPS_ERR_STRIDE
+    assert bok(c_bs=16) == rp.REPOPS_ERR_STRIDE          # batches overlap in C
+    assert bok(c_bs=0) == rp.REPOPS_ERR_STRIDE           # all batches on one C
+    assert bok(C=PA + 4 * 100) == rp.REPOPS_ERR_ALIAS    # C inside A's batches
+    assert bok(bias=PC + 8) == rp.REPOPS_ERR_ALIAS       # bias inside C
+    assert bok(bias=PB, bias_s=-1) == rp.REPOPS_ERR_STRIDE
+    assert bok(variant=999) == rp.REPOPS_ERR_VARIANT
+    assert bok(batch=0, A=0, B=0, C=0) == rp.REPOPS_OK   # nothing to do
+
+
+def test_batched_injectivity_rule():
+    # interleaved heads: C viewed as (batch=4, M=8, N=16) inside an (8, 4*16)
+    # row-major buffer: c_bs=16, c_rs=64, c_cs=1 is injective
+    assert rp.repops_check_args_f32(PA, 64, 1, PB, 16, 1, PC, 64, 1, 8, 16, 64, 0, 0, -1) == 0
+    # (C placed inside A, so each call stops with an error before any launch;
+    # the alias check comes after the stride check)
+    st = rp.repops_matmul_batched_f32(PA, 0, 64, 1, PB, 0, 16, 1, PA, 16, 64, 1, 8, 16, 64, 4,
+                                      0, 0, None, 0, 0, 0, -1)
+    assert st == rp.REPOPS_ERR_ALIAS    # strides accepted, stopped by the alias check
+    st = rp.repops_matmul_batched_f32(PA, 0, 64, 1, PB, 0, 16, 1, PA, 15, 64, 1, 8, 16, 64, 4,
+                                      0, 0, None, 0, 0, 0, -1)
+    assert st == rp.REPOPS_ERR_STRIDE   # batch stride 15 < 16 columns: overlap
