@@ -130,6 +130,8 @@ def main():
     dev = torch.device("cuda:0")
     if args.workload in inputs.FOLD_WORKLOADS:
         return bench_fold(args, torch, rp, inputs, dev)
+    if args.workload in inputs.BATCHED_WORKLOADS:
+        return bench_batched(args, torch, rp, inputs, dev)
     w = inputs.WORKLOADS[args.workload]
     log("workload %s: %s" % (w.name, w.description))
     A, B = inputs.make_operands(w.name)
@@ -259,6 +261,77 @@ def main():
                       "min": round(min(kernel_ms), 4), "max": round(max(kernel_ms), 4)},
     }
     rec.update(extra)
+    print(json.dumps(rec), flush=True)
+
+
+def bench_batched(args, torch, rp, inputs, dev):
+    """Batched fixed-order products (attention-shaped): one step = one C-ABI
+    call over all heads; TFLOP/s and the same ALU roofline as the GEMM."""
+    import oracle
+    w = inputs.BATCHED_WORKLOADS[args.workload]
+    log("batched workload %s: %s" % (w.name, w.description))
+    A, B = inputs.make_batched_operands(w.name)
+    ga = torch.from_numpy(A).to(dev)
+    gb = torch.from_numpy(B).to(dev)
+    out = torch.empty((w.batch, w.M, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    variant = args.variant if args.variant is None or not args.variant.isdigit() else int(args.variant)
+
+    def step():
+        rp.matmul_batched(ga, gb, trans_a=w.trans_a, trans_b=w.trans_b, out=out,
+                          variant=variant, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        starts[s].record(stream)
+        step()
+        ends[s].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [starts[s].elapsed_time(ends[s]) for s in range(args.steps)]
+    log("per-step kernel ms: " + " ".join("%.4f" % t for t in kernel_ms))
+    C = out.cpu().numpy()
+    for h in range(0, w.batch, 5):
+        ii, jj = inputs.sample_entries(w.M, w.N, 64, 77 + h)
+        want = oracle.entries_f32(A[h], B[h], ii, jj, w.trans_a, w.trans_b)
+        if not np.array_equal(C[h][ii, jj].view(np.uint32), want.view(np.uint32)):
+            print("bench.py: batched output differs from the oracle; no number is reported",
+                  file=sys.stderr)
+            sys.exit(3)
+    log("bit-exact on sampled outputs of every fifth head")
+    flops = float(w.flops)
+    ms_per_step = wall * 1e3 / args.steps
+    k_avg = float(np.mean(kernel_ms))
+    achieved = flops / (k_avg * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.perf_counter()
+        rows = 64
+        oracle.matmul_f32(A[0][:rows] if not w.trans_a else A[0][:, :rows], B[0],
+                          w.trans_a, w.trans_b, nthreads=cpu_threads())
+        dt = time.perf_counter() - t0
+        cpu = {"value": 2.0 * rows * w.N * w.K / dt / 1e12, "unit": "TFLOP/s",
+               "cores": cpu_threads(), "kind": "oracle",
+               "sample": "rows 0..%d of head 0 in %.2f s" % (rows - 1, dt)}
+    rec = {
+        "metric": "fixed-order batched FP32 matmul TFLOP/s, bit-exact",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 4), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "strong", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded numpy PCG64)",
+        "config": {"workload": "%s batch=%d M=%d N=%d K=%d" % (w.name, w.batch, w.M, w.N, w.K)},
+        "roofline": {"bound": "alu", "achieved": round(achieved, 4), "peak": UNFUSED_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / UNFUSED_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu, "bitexact_sampled": True,
+        "kernel_ms": {"mean": round(k_avg, 4), "median": round(float(np.median(kernel_ms)), 4),
+                      "min": round(min(kernel_ms), 4), "max": round(max(kernel_ms), 4)},
+    }
     print(json.dumps(rec), flush=True)
 
 
