@@ -100,8 +100,12 @@ def cpu_baseline(A, B, w, target_s):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20 for a matmul, 100 for the sub-millisecond "
+                         "batched and fold steps)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before timing (default 5 for a matmul, 200 for the "
+                         "batched and fold steps, enough for the clock to settle)")
     ap.add_argument("--workload", default="llama8b_mlp_up",
                     help="a matmul workload (default: the Llama-8B up-projection) or a "
                          "fold workload (fixed-order gradient average + SGD step)")
@@ -112,6 +116,13 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
+    from bit_reproducible_fp32_amd import inputs
+
+    short = args.workload not in inputs.WORKLOADS
+    if args.steps is None:
+        args.steps = 100 if short else 20
+    if args.warmup is None:
+        args.warmup = 200 if short else 5
 
     if args.gpus != 1:
         print("bench.py measures one GPU only: the fixed-order matmul shards over output "
@@ -121,7 +132,6 @@ def main():
 
     import torch
     import bit_reproducible_fp32_amd as rp
-    from bit_reproducible_fp32_amd import inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

@@ -20,6 +20,9 @@ gradual underflow, ``sum`` starting at +0.0:
   1995), vectorised over (i, j);
 * :func:`exact_matmul` -- exact rational arithmetic with a hand-written
   binary32 round-to-nearest-even rounder; no hardware floating point.
+
+The submodule :mod:`oracle.merkle` holds the tensor hash (SHA-256 in an
+RFC 6962 Merkle tree) and the referee's re-execution of a disputed matmul.
 """
 from __future__ import annotations
 
