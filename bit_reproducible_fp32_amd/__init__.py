@@ -17,6 +17,7 @@ from __future__ import annotations
 from ._lib import (  # noqa: F401
     EXPORTS,
     REPOPS_ERR_ALIAS,
+    REPOPS_ERR_ALIGN,
     REPOPS_ERR_DIM,
     REPOPS_ERR_DUPLICATE,
     REPOPS_FOLD_MAX_PER_PASS,
@@ -24,6 +25,8 @@ from ._lib import (  # noqa: F401
     REPOPS_ERR_NULL,
     REPOPS_ERR_STRIDE,
     REPOPS_ERR_VARIANT,
+    REPOPS_ERR_WORKSPACE,
+    REPOPS_MERKLE_DEFAULT_LEAF_BYTES,
     REPOPS_OK,
     RepopsError,
     load,
@@ -34,7 +37,10 @@ from ._lib import (  # noqa: F401
     repops_matmul_batched_f32,
     repops_matmul_f32,
     repops_matmul_f32_ex,
+    repops_merkle_root,
+    repops_merkle_workspace_bytes,
     repops_pick_variant_f32,
+    repops_referee_matmul_f32,
     repops_strerror,
     repops_variant_count,
     repops_variant_name,
@@ -205,3 +211,93 @@ def fold_mean_sgd(grads, theta, eta, *, dids=None, gbar=None, stream=None):
     if st != REPOPS_OK:
         raise RepopsError(st, "repops_fold_mean_sgd_f32")
     return gbar
+
+
+def _workspace(nbytes, leaf_bytes, device, workspace):
+    import torch
+
+    need = repops_merkle_workspace_bytes(nbytes, leaf_bytes)
+    if need < 0:
+        raise ValueError("invalid sizes: %d bytes in leaves of %d (both multiples of 4, "
+                         "leaf_bytes in [4, 2^24])" % (nbytes, leaf_bytes))
+    if need == 0:
+        return None, 0
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < need or not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous with at least %d bytes" % need)
+        return workspace, workspace.numel() * workspace.element_size()
+    return torch.empty(need, dtype=torch.uint8, device=device), need
+
+
+def merkle_root(t, *, leaf_bytes: int = REPOPS_MERKLE_DEFAULT_LEAF_BYTES, out=None,
+                workspace=None, stream=None):
+    """SHA-256 Merkle tree hash (RFC 6962 shape) of a contiguous CUDA tensor's
+    bytes, computed on the GPU.  For a float32 tensor this is the tensor hash
+    of its elements in row-major order.  With ``out`` (a 32-byte uint8 CUDA
+    tensor) the root is written there and nothing is synchronised; otherwise
+    the 32 root bytes are returned as ``bytes``."""
+    import torch
+
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("t must be a CUDA tensor; this library has no CPU path")
+    if not t.is_contiguous():
+        raise ValueError("t must be contiguous (the hash covers its row-major bytes)")
+    nbytes = t.numel() * t.element_size()
+    ws, ws_bytes = _workspace(nbytes, leaf_bytes, t.device, workspace)
+    root = out if out is not None else torch.empty(32, dtype=torch.uint8, device=t.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    with torch.cuda.device(t.device):
+        st = repops_merkle_root(t.data_ptr() if nbytes else None, nbytes, leaf_bytes,
+                                ws.data_ptr() if ws is not None else None, ws_bytes,
+                                root.data_ptr(), stream.cuda_stream)
+    if st != REPOPS_OK:
+        raise RepopsError(st, "repops_merkle_root")
+    if out is not None:
+        return out
+    stream.synchronize()
+    return bytes(root.cpu().numpy().tobytes())
+
+
+def referee_matmul(a, b, claims, *, trans_a: bool = False, trans_b: bool = False,
+                   leaf_bytes: int = REPOPS_MERKLE_DEFAULT_LEAF_BYTES, out=None, workspace=None,
+                   stream=None):
+    """The referee's decision on a disputed matmul output: recompute
+    C = op(a) op(b) on the GPU, hash it, and compare with each trainer's
+    claimed 32-byte output hash.  Returns (root bytes, [bool per claim], C)."""
+    import numpy as np
+    import torch
+
+    for name, t in (("a", a), ("b", b)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2 or t.dtype != torch.float32:
+            raise TypeError("%s must be a 2-D float32 tensor" % name)
+        if not t.is_cuda:
+            raise ValueError("%s must be on a GPU; this library has no CPU path" % name)
+    M, N, K = _logical(a, b, trans_a, trans_b)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    elif tuple(out.shape) != (M, N) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 (%d, %d) tensor" % (M, N))
+    claims = [bytes(c) for c in claims]
+    if any(len(c) != 32 for c in claims):
+        raise ValueError("each claim is a 32-byte digest")
+    dev = a.device
+    ws, ws_bytes = _workspace(M * N * 4, leaf_bytes, dev, workspace)
+    cl = (torch.from_numpy(np.frombuffer(b"".join(claims), dtype=np.uint8).copy()).to(dev)
+          if claims else None)
+    root = torch.empty(32, dtype=torch.uint8, device=dev)
+    match = torch.empty(max(len(claims), 1), dtype=torch.int32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    with torch.cuda.device(dev):
+        st = repops_referee_matmul_f32(a.data_ptr(), a.stride(0), a.stride(1), b.data_ptr(),
+                                       b.stride(0), b.stride(1), out.data_ptr(), M, N, K,
+                                       trans_a, trans_b, leaf_bytes,
+                                       ws.data_ptr() if ws is not None else None, ws_bytes,
+                                       cl.data_ptr() if cl is not None else None, len(claims),
+                                       root.data_ptr(), match.data_ptr(), stream.cuda_stream)
+    if st != REPOPS_OK:
+        raise RepopsError(st, "repops_referee_matmul_f32")
+    stream.synchronize()
+    return (bytes(root.cpu().numpy().tobytes()),
+            [bool(v) for v in match.cpu().numpy()[:len(claims)]], out)

@@ -20,7 +20,10 @@ REPOPS_ERR_ALIAS = 4
 REPOPS_ERR_VARIANT = 5
 REPOPS_ERR_HIP = 6
 REPOPS_ERR_DUPLICATE = 7
+REPOPS_ERR_ALIGN = 8
+REPOPS_ERR_WORKSPACE = 9
 REPOPS_FOLD_MAX_PER_PASS = 64
+REPOPS_MERKLE_DEFAULT_LEAF_BYTES = 1024
 
 EXPORTS = (
     "repops_matmul_f32",
@@ -34,6 +37,9 @@ EXPORTS = (
     "repops_build_manifest",
     "repops_canonical_order",
     "repops_fold_mean_sgd_f32",
+    "repops_merkle_workspace_bytes",
+    "repops_merkle_root",
+    "repops_referee_matmul_f32",
 )
 
 _lib = None
@@ -81,6 +87,13 @@ def load():
     lib.repops_canonical_order.restype = ci
     lib.repops_fold_mean_sgd_f32.argtypes = [vp, i64, i64, ctypes.c_float, vp, vp, vp]
     lib.repops_fold_mean_sgd_f32.restype = ci
+    lib.repops_merkle_workspace_bytes.argtypes = [i64, i64]
+    lib.repops_merkle_workspace_bytes.restype = i64
+    lib.repops_merkle_root.argtypes = [vp, i64, i64, vp, i64, vp, vp]
+    lib.repops_merkle_root.restype = ci
+    lib.repops_referee_matmul_f32.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i64, i64, ci,
+                                              ci, i64, vp, i64, vp, i64, vp, vp, vp]
+    lib.repops_referee_matmul_f32.restype = ci
     _lib = lib
     return lib
 
@@ -153,6 +166,24 @@ def repops_fold_mean_sgd_f32(grads, k, d, eta, theta, gbar, stream) -> int:
     arr = (ctypes.c_void_p * max(int(k), 1))(*[int(g) for g in grads])
     return load().repops_fold_mean_sgd_f32(ctypes.cast(arr, ctypes.c_void_p), int(k), int(d),
                                            float(eta), theta, gbar, stream)
+
+
+def repops_merkle_workspace_bytes(nbytes, leaf_bytes) -> int:
+    return load().repops_merkle_workspace_bytes(int(nbytes), int(leaf_bytes))
+
+
+def repops_merkle_root(data, nbytes, leaf_bytes, workspace, workspace_bytes, root, stream) -> int:
+    return load().repops_merkle_root(data, int(nbytes), int(leaf_bytes), workspace,
+                                     int(workspace_bytes), root, stream)
+
+
+def repops_referee_matmul_f32(A, a_rs, a_cs, B, b_rs, b_cs, C, M, N, K, trans_a, trans_b,
+                              leaf_bytes, workspace, workspace_bytes, claims, nclaims, root, match,
+                              stream) -> int:
+    return load().repops_referee_matmul_f32(A, a_rs, a_cs, B, b_rs, b_cs, C, M, N, K,
+                                            int(trans_a), int(trans_b), int(leaf_bytes),
+                                            workspace, int(workspace_bytes), claims, int(nclaims),
+                                            root, match, stream)
 
 
 strerror = repops_strerror

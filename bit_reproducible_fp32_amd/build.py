@@ -24,9 +24,11 @@ ASM = os.path.join(HERE, "librepops_gfx950.s")
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-KERNEL_SOURCES = [os.path.join(CSRC, "repops_kernels.hip"), os.path.join(CSRC, "repops_fold.hip")]
+KERNEL_SOURCES = [os.path.join(CSRC, "repops_kernels.hip"), os.path.join(CSRC, "repops_fold.hip"),
+                  os.path.join(CSRC, "repops_merkle.hip")]
 SOURCES = KERNEL_SOURCES + [os.path.join(CSRC, "repops_api.cpp"),
-                            os.path.join(CSRC, "repops_fold_api.cpp")]
+                            os.path.join(CSRC, "repops_fold_api.cpp"),
+                            os.path.join(CSRC, "repops_merkle_api.cpp")]
 
 FP_FLAGS = ["-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero"]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -310,6 +310,8 @@ const char* repops_strerror(repops_status status) {
         case REPOPS_ERR_VARIANT: return "unknown kernel variant";
         case REPOPS_ERR_HIP: return "HIP launch error";
         case REPOPS_ERR_DUPLICATE: return "two contributors share one identity";
+        case REPOPS_ERR_ALIGN: return "a pointer is not aligned as the call requires";
+        case REPOPS_ERR_WORKSPACE: return "the workspace is missing or too small";
     }
     return "unknown status";
 }

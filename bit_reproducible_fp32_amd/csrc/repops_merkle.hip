@@ -1,0 +1,327 @@
+// gfx950 kernels for the tensor hash that trainers attach to every operator
+// output and that the referee recomputes when an output hash is disputed
+// (Verde and RepOps article, sections 2.3.1, 2.3.2 and 2.4, case 3).
+//
+// The hash is SHA-256 (FIPS 180-4, sections 4.1.2, 4.2.2, 5.1.1, 5.3.3 and
+// 6.2) in the Merkle tree of RFC 6962, section 2.1:
+//     leaf  = SHA-256(0x00 || leaf bytes)
+//     node  = SHA-256(0x01 || left digest || right digest)
+//     the left subtree of n leaves holds the largest power of two below n,
+//     and the empty input hashes to SHA-256 of the empty string.
+// That recursive shape is the same tree as pairing neighbours level by level,
+// bottom up, with an unpaired last node carried up unchanged: the left part
+// of every split is a perfect, aligned subtree.  The kernels build it that
+// way.
+//
+// One lane hashes one leaf (SHA-256 is a serial chain of compressions; the
+// leaves are the parallel dimension).  A workgroup of kGroup lanes then
+// folds its kGroup neighbouring leaf digests eight levels up the tree in LDS,
+// so one launch turns n leaves into ceil(n / 256) digests; each later launch
+// does the same to the digests, until one is left.  Groups start at multiples
+// of 256 nodes, so a group's fold is exactly a subtree of the global tree.
+//
+// Everything is 32-bit integer arithmetic; there is no floating point here.
+#include <hip/hip_runtime.h>
+
+#include "repops_internal.h"
+
+namespace repops {
+namespace {
+
+constexpr int kGroup = 256;
+
+// FIPS 180-4, section 4.2.2: the first 32 bits of the fractional parts of
+// the cube roots of the first 64 primes.
+constexpr uint32_t kRound[64] = {
+    0x428a2f98u, 0x71374491u, 0xb5c0fbcfu, 0xe9b5dba5u, 0x3956c25bu, 0x59f111f1u, 0x923f82a4u,
+    0xab1c5ed5u, 0xd807aa98u, 0x12835b01u, 0x243185beu, 0x550c7dc3u, 0x72be5d74u, 0x80deb1feu,
+    0x9bdc06a7u, 0xc19bf174u, 0xe49b69c1u, 0xefbe4786u, 0x0fc19dc6u, 0x240ca1ccu, 0x2de92c6fu,
+    0x4a7484aau, 0x5cb0a9dcu, 0x76f988dau, 0x983e5152u, 0xa831c66du, 0xb00327c8u, 0xbf597fc7u,
+    0xc6e00bf3u, 0xd5a79147u, 0x06ca6351u, 0x14292967u, 0x27b70a85u, 0x2e1b2138u, 0x4d2c6dfcu,
+    0x53380d13u, 0x650a7354u, 0x766a0abbu, 0x81c2c92eu, 0x92722c85u, 0xa2bfe8a1u, 0xa81a664bu,
+    0xc24b8b70u, 0xc76c51a3u, 0xd192e819u, 0xd6990624u, 0xf40e3585u, 0x106aa070u, 0x19a4c116u,
+    0x1e376c08u, 0x2748774cu, 0x34b0bcb5u, 0x391c0cb3u, 0x4ed8aa4au, 0x5b9cca4fu, 0x682e6ff3u,
+    0x748f82eeu, 0x78a5636fu, 0x84c87814u, 0x8cc70208u, 0x90befffau, 0xa4506cebu, 0xbef9a3f7u,
+    0xc67178f2u};
+
+// FIPS 180-4, section 5.3.3: the first 32 bits of the fractional parts of
+// the square roots of the first 8 primes.
+constexpr uint32_t kInit[8] = {0x6a09e667u, 0xbb67ae85u, 0x3c6ef372u, 0xa54ff53au,
+                               0x510e527fu, 0x9b05688cu, 0x1f83d9abu, 0x5be0cd19u};
+
+__host__ __device__ __forceinline__ uint32_t rotr(uint32_t x, int n) { return (x >> n) | (x << (32 - n)); }
+
+__host__ __device__ __forceinline__ uint32_t bswap32(uint32_t x) { return __builtin_bswap32(x); }
+
+__host__ __device__ __forceinline__ void init_state(uint32_t (&h)[8]) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) h[q] = kInit[q];
+}
+
+// FIPS 180-4, section 6.2.2: one compression of the 16-word block w (big-endian
+// words of the message) into h.  The message schedule runs in place in w.
+__host__ __device__ __forceinline__ void compress(uint32_t (&h)[8], uint32_t (&w)[16]) {
+    uint32_t a = h[0], b = h[1], c = h[2], d = h[3], e = h[4], f = h[5], g = h[6], hh = h[7];
+#pragma unroll
+    for (int t = 0; t < 64; ++t) {
+        uint32_t wt;
+        if (t < 16) {
+            wt = w[t];
+        } else {
+            const uint32_t w15 = w[(t - 15) & 15], w2 = w[(t - 2) & 15];
+            const uint32_t s0 = rotr(w15, 7) ^ rotr(w15, 18) ^ (w15 >> 3);
+            const uint32_t s1 = rotr(w2, 17) ^ rotr(w2, 19) ^ (w2 >> 10);
+            wt = w[t & 15] + s0 + w[(t - 7) & 15] + s1;
+            w[t & 15] = wt;
+        }
+        const uint32_t S1 = rotr(e, 6) ^ rotr(e, 11) ^ rotr(e, 25);
+        const uint32_t ch = (e & f) ^ (~e & g);
+        const uint32_t t1 = hh + S1 + ch + kRound[t] + wt;
+        const uint32_t S0 = rotr(a, 2) ^ rotr(a, 13) ^ rotr(a, 22);
+        const uint32_t maj = (a & b) ^ (a & c) ^ (b & c);
+        const uint32_t t2 = S0 + maj;
+        hh = g;
+        g = f;
+        f = e;
+        e = d + t1;
+        d = c;
+        c = b;
+        b = a;
+        a = t1 + t2;
+    }
+    h[0] += a;
+    h[1] += b;
+    h[2] += c;
+    h[3] += d;
+    h[4] += e;
+    h[5] += f;
+    h[6] += g;
+    h[7] += hh;
+}
+
+// Message word of the leaf message 0x00 || data: its top byte is the last
+// byte of the previous data word (0 before the first, the prefix byte), its
+// other three bytes the first three of data word d.  Data words are read as
+// stored (little-endian), message words are big-endian.
+__host__ __device__ __forceinline__ uint32_t shifted_word(uint32_t prev, uint32_t d) {
+    return (prev & 0xff000000u) | (bswap32(d) >> 8);
+}
+
+// SHA-256(0x00 || the nw words at p): message length 4*nw + 1 bytes.
+// VEC: p is 16-byte aligned, full blocks are read as four 16-byte loads.
+template <bool VEC>
+__host__ __device__ __forceinline__ void hash_leaf(const uint32_t* __restrict__ p, int64_t nw,
+                                          uint32_t (&h)[8]) {
+    init_state(h);
+    uint32_t prev = 0;
+    const int64_t full = nw >> 4;  // blocks made only of data-derived words
+    for (int64_t blk = 0; blk < full; ++blk) {
+        uint32_t d[16], w[16];
+        const uint32_t* q = p + (blk << 4);
+        if constexpr (VEC) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const uint4 x = *reinterpret_cast<const uint4*>(q + 4 * v);
+                d[4 * v] = x.x;
+                d[4 * v + 1] = x.y;
+                d[4 * v + 2] = x.z;
+                d[4 * v + 3] = x.w;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) d[j] = q[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            w[j] = shifted_word(prev, d[j]);
+            prev = d[j];
+        }
+        compress(h, w);
+    }
+    // The rest: remaining data words, the 0x80 terminator right after the
+    // last data byte, zeros, and the 64-bit bit length in the last two words
+    // (FIPS 180-4, section 5.1.1).  One or two blocks.
+    const uint64_t bits = (static_cast<uint64_t>(nw) * 4 + 1) * 8;
+    const int64_t nblocks = (nw * 4 + 1 + 9 + 63) >> 6;
+    const int64_t last = (nblocks << 4) - 1;
+    for (int64_t blk = full; blk < nblocks; ++blk) {
+        uint32_t w[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int64_t t = (blk << 4) + j;
+            uint32_t v = 0;
+            if (t < nw) {
+                const uint32_t d = p[t];
+                v = shifted_word(prev, d);
+                prev = d;
+            } else if (t == nw) {
+                v = (prev & 0xff000000u) | 0x00800000u;
+            }
+            if (t == last - 1) v = static_cast<uint32_t>(bits >> 32);
+            if (t == last) v = static_cast<uint32_t>(bits);
+            w[j] = v;
+        }
+        compress(h, w);
+    }
+}
+
+// SHA-256(0x01 || l || r) for two digests (65 bytes, two blocks).
+__host__ __device__ __forceinline__ void hash_node(const uint32_t (&l)[8], const uint32_t (&r)[8],
+                                          uint32_t (&h)[8]) {
+    uint32_t w[16];
+    init_state(h);
+    w[0] = 0x01000000u | (l[0] >> 8);
+#pragma unroll
+    for (int j = 1; j < 8; ++j) w[j] = (l[j - 1] << 24) | (l[j] >> 8);
+    w[8] = (l[7] << 24) | (r[0] >> 8);
+#pragma unroll
+    for (int j = 9; j < 16; ++j) w[j] = (r[j - 9] << 24) | (r[j - 8] >> 8);
+    compress(h, w);
+    w[0] = (r[7] << 24) | 0x00800000u;
+#pragma unroll
+    for (int j = 1; j < 15; ++j) w[j] = 0;
+    w[15] = 65 * 8;
+    compress(h, w);
+}
+
+// One stage.  LEAF: item i is leaf i of the data (words [i*leaf_words,
+// min((i+1)*leaf_words, total_words))); otherwise item i is the digest
+// src[8i .. 8i+7].  Writes one digest per workgroup to dst[8*blockIdx.x ..];
+// FINAL (a single workgroup): the root, as the digest's 32 bytes.
+template <bool LEAF, bool VEC, bool FINAL>
+__global__ __launch_bounds__(kGroup) void repops_merkle_kernel(const uint32_t* __restrict__ src,
+                                                               int64_t n_items, int64_t leaf_words,
+                                                               int64_t total_words,
+                                                               uint32_t* __restrict__ dst) {
+    __shared__ uint32_t node[8][kGroup];
+    const int tid = static_cast<int>(threadIdx.x);
+    const int64_t first = static_cast<int64_t>(blockIdx.x) * kGroup;
+    const int64_t rem = n_items - first;
+    const int count = rem < kGroup ? static_cast<int>(rem) : kGroup;
+
+    uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (tid < count) {
+        const int64_t item = first + tid;
+        if constexpr (LEAF) {
+            const int64_t w0 = item * leaf_words;
+            const int64_t left = total_words - w0;
+            hash_leaf<VEC>(src + w0, left < leaf_words ? left : leaf_words, h);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) h[q] = src[item * 8 + q];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) node[q][tid] = h[q];
+    }
+    // Level by level: the node at lane tid (a multiple of 2*half) takes its
+    // right neighbour at tid + half if there is one, else is carried up.
+    for (int half = 1; half < count; half *= 2) {
+        __syncthreads();
+        if ((tid & (2 * half - 1)) == 0 && tid + half < count) {
+            uint32_t r[8], out[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) r[q] = node[q][tid + half];
+            hash_node(h, r, out);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                h[q] = out[q];
+                node[q][tid] = out[q];
+            }
+        }
+    }
+    if (tid == 0) {
+        uint32_t* o = dst + static_cast<int64_t>(blockIdx.x) * 8;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) o[q] = FINAL ? bswap32(h[q]) : h[q];
+    }
+}
+
+// SHA-256 of the empty message (the empty tree), written as 32 bytes.
+__global__ __launch_bounds__(64) void repops_merkle_empty_kernel(uint32_t* __restrict__ root) {
+    uint32_t h[8], w[16];
+    init_state(h);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) w[j] = 0;
+    w[0] = 0x80000000u;
+    compress(h, w);
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) root[q] = bswap32(h[q]);
+    }
+}
+
+// match[c] = 1 when the 32 bytes of claim c equal the root, else 0.
+__global__ __launch_bounds__(256) void repops_merkle_match_kernel(const uint32_t* __restrict__ root,
+                                                                  const uint32_t* __restrict__ claims,
+                                                                  int64_t nclaims,
+                                                                  int32_t* __restrict__ match) {
+    const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (c >= nclaims) return;
+    uint32_t diff = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) diff |= root[q] ^ claims[c * 8 + q];
+    match[c] = diff == 0 ? 1 : 0;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+}  // namespace
+
+int64_t merkle_workspace_bytes(int64_t n_leaves) {
+    // Two ping-pong buffers: the first stage's digests and the second's; later
+    // stages alternate between them (each is consumed before it is refilled).
+    if (n_leaves <= kGroup) return 0;
+    const int64_t n1 = ceil_div(n_leaves, kGroup);
+    const int64_t n2 = ceil_div(n1, kGroup);
+    return round_up(n1 * 32, 256) + (n2 > 1 ? round_up(n2 * 32, 256) : 0);
+}
+
+int launch_merkle_root(const uint32_t* data, int64_t total_words, int64_t leaf_words, void* ws,
+                       uint32_t* root, bool vec, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (total_words == 0) {
+        hipLaunchKernelGGL(repops_merkle_empty_kernel, dim3(1), dim3(64), 0, s, root);
+        return static_cast<int>(hipGetLastError());
+    }
+    const int64_t n_leaves = ceil_div(total_words, leaf_words);
+    const int64_t n1 = ceil_div(n_leaves, kGroup);
+    uint32_t* buf[2] = {static_cast<uint32_t*>(ws), nullptr};
+    if (n1 > 1) buf[1] = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + round_up(n1 * 32, 256));
+
+    using Fn = void (*)(const uint32_t*, int64_t, int64_t, int64_t, uint32_t*);
+    int64_t n = n_leaves;
+    const uint32_t* src = data;
+    for (int stage = 0;; ++stage) {
+        const int64_t blocks = ceil_div(n, kGroup);
+        const bool final_stage = blocks == 1;
+        uint32_t* dst = final_stage ? root : buf[stage & 1];
+        Fn fn;
+        if (stage == 0)
+            fn = final_stage ? (vec ? repops_merkle_kernel<true, true, true>
+                                    : repops_merkle_kernel<true, false, true>)
+                             : (vec ? repops_merkle_kernel<true, true, false>
+                                    : repops_merkle_kernel<true, false, false>);
+        else
+            fn = final_stage ? repops_merkle_kernel<false, false, true>
+                             : repops_merkle_kernel<false, false, false>;
+        hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(kGroup), 0, s, src, n,
+                           leaf_words, total_words, dst);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return static_cast<int>(err);
+        if (final_stage) return 0;
+        src = dst;
+        n = blocks;
+    }
+}
+
+int launch_merkle_match(const uint32_t* root, const uint32_t* claims, int64_t nclaims,
+                        int32_t* match, void* stream) {
+    if (nclaims == 0) return 0;
+    hipLaunchKernelGGL(repops_merkle_match_kernel, dim3(static_cast<unsigned>(ceil_div(nclaims, 256))),
+                       dim3(256), 0, static_cast<hipStream_t>(stream), root, claims, nclaims, match);
+    return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace repops

@@ -37,7 +37,8 @@
  * argument errors are detected on the host before anything is queued, and
  * then nothing is written.  Launch failures are reported as REPOPS_ERR_HIP;
  * faults during execution surface at the caller's next synchronisation.
- * No entry point synchronises the stream.
+ * No entry point synchronises the stream.  The calls that need device scratch
+ * (the tensor hash) take it from the caller as a workspace argument.
  */
 #ifndef REPOPS_H
 #define REPOPS_H
@@ -58,7 +59,9 @@ typedef enum repops_status {
     REPOPS_ERR_ALIAS = 4,   /* the bytes C spans overlap those of A or B */
     REPOPS_ERR_VARIANT = 5, /* unknown variant index */
     REPOPS_ERR_HIP = 6,     /* the HIP runtime reported an error at launch */
-    REPOPS_ERR_DUPLICATE = 7 /* two contributors share one identity */
+    REPOPS_ERR_DUPLICATE = 7, /* two contributors share one identity */
+    REPOPS_ERR_ALIGN = 8,   /* a pointer is not aligned as the call requires */
+    REPOPS_ERR_WORKSPACE = 9 /* the workspace is NULL or smaller than required */
 } repops_status;
 
 /*
@@ -196,6 +199,79 @@ repops_status repops_canonical_order(const uint8_t* const* dids, const int64_t* 
  */
 repops_status repops_fold_mean_sgd_f32(const float* const* grads, int64_t k, int64_t d,
                                        float eta, float* theta, float* gbar, void* stream);
+
+/* ---- Tensor hash and the referee's single-operator re-execution ----------
+ *
+ * Verde and RepOps article, section 2.3.1 (every node of the training
+ * graph carries hash lists of its input and output tensors), section 2.3.2
+ * (checkpoint hashes are Merkle trees) and section 2.4, case 3 (when two
+ * trainers agree on a node's inputs but not on its output hash, the referee
+ * runs that one operator and sees which output hash it reproduces).  The
+ * article names no hash function.  These calls use SHA-256 (FIPS 180-4) in
+ * the Merkle tree of RFC 6962, section 2.1:
+ *     leaf hash  SHA-256(0x00 || leaf bytes)
+ *     node hash  SHA-256(0x01 || left digest || right digest)
+ *     the left subtree of n > 1 leaves holds the largest power of two < n
+ *     the empty input hashes to SHA-256 of the empty string.
+ * The data is cut into leaves of leaf_bytes from its first byte, the last
+ * leaf shorter when nbytes is not a multiple.  A float32 tensor is hashed as
+ * its elements in logical row-major order, each in little-endian binary32
+ * encoding: the bytes of a contiguous row-major tensor on this device.
+ * The root is written to device memory as the 32 digest bytes.
+ */
+
+/* The leaf size the Python binding uses when none is given. */
+#define REPOPS_MERKLE_DEFAULT_LEAF_BYTES 1024
+
+/*
+ * Bytes of device workspace repops_merkle_root needs for nbytes of data in
+ * leaves of leaf_bytes (0 when the tree fits one workgroup, i.e. at most 256
+ * leaves), or -1 when the sizes are invalid (see repops_merkle_root).  Host
+ * only; touches no device.
+ */
+int64_t repops_merkle_workspace_bytes(int64_t nbytes, int64_t leaf_bytes);
+
+/*
+ * root = the Merkle tree hash above of the nbytes bytes at data, queued on
+ * `stream`.  data: device, 4-byte aligned (16-byte aligned with leaf_bytes a
+ * multiple of 16 takes the wide-load path; the hash is the same).  nbytes:
+ * a multiple of 4 in [0, 2^50].  leaf_bytes: a multiple of 4 in [4, 2^24].
+ * workspace: device, 16-byte aligned, at least
+ * repops_merkle_workspace_bytes(nbytes, leaf_bytes) bytes (may be NULL when
+ * that is 0); its contents are scratch, overwritten.  root: device, 32
+ * bytes, 4-byte aligned.  All are borrowed until the queued work completes;
+ * calls that share a workspace must be ordered on one stream.
+ * Errors: REPOPS_ERR_DIM (sizes out of range or not multiples of 4),
+ * REPOPS_ERR_NULL (root NULL, or data NULL with nbytes > 0),
+ * REPOPS_ERR_ALIGN, REPOPS_ERR_WORKSPACE, REPOPS_ERR_ALIAS (root, workspace
+ * and data overlap), REPOPS_ERR_HIP.
+ */
+repops_status repops_merkle_root(const void* data, int64_t nbytes, int64_t leaf_bytes,
+                                 void* workspace, int64_t workspace_bytes, void* root,
+                                 void* stream);
+
+/*
+ * The referee's decision on an output-hash dispute over a matmul: queue
+ * C = op(A) op(B) (repops_matmul_f32 with C contiguous row-major, c_rs = N,
+ * c_cs = 1), root = the tensor hash of C with leaves of leaf_bytes, and
+ * match[c] = 1 if claim c (32 bytes at claims + 32*c) equals root, else 0,
+ * for c < nclaims.  A trainer's claim that is not reproduced is wrong; when
+ * none is, both trainers are.  Everything is device memory and queued on
+ * `stream`; nothing is synchronised.  A, B, C, M, N, K, trans_a, trans_b as
+ * in repops_matmul_f32; workspace as in repops_merkle_root for nbytes =
+ * 4*M*N.  claims: device, 4-byte aligned (may be NULL when nclaims == 0).
+ * root: device, 32 bytes.  match: device, nclaims int32 values.
+ * Errors: those of repops_matmul_f32 and repops_merkle_root, plus
+ * REPOPS_ERR_DIM (nclaims < 0 or above 2^40), REPOPS_ERR_NULL (claims or
+ * match NULL with nclaims > 0), REPOPS_ERR_ALIGN and REPOPS_ERR_ALIAS (match,
+ * claims, root, C and the workspace overlap).
+ */
+repops_status repops_referee_matmul_f32(const float* A, int64_t a_rs, int64_t a_cs, const float* B,
+                                        int64_t b_rs, int64_t b_cs, float* C, int64_t M, int64_t N,
+                                        int64_t K, int trans_a, int trans_b, int64_t leaf_bytes,
+                                        void* workspace, int64_t workspace_bytes,
+                                        const void* claims, int64_t nclaims, void* root,
+                                        int32_t* match, void* stream);
 
 #ifdef __cplusplus
 }
