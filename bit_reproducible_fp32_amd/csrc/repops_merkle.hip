@@ -14,11 +14,20 @@
 // way.
 //
 // One lane hashes one leaf (SHA-256 is a serial chain of compressions; the
-// leaves are the parallel dimension).  A workgroup of kGroup lanes then
-// folds its kGroup neighbouring leaf digests eight levels up the tree in LDS,
-// so one launch turns n leaves into ceil(n / 256) digests; each later launch
-// does the same to the digests, until one is left.  Groups start at multiples
-// of 256 nodes, so a group's fold is exactly a subtree of the global tree.
+// leaves are the parallel dimension).  A workgroup of kLeafGroup lanes then
+// folds its neighbouring leaf digests up the tree in LDS, so the first launch
+// turns n leaves into ceil(n / 256) digests; each later launch folds groups of
+// kNodeGroup digests the same way, until one is left.  Groups start at
+// multiples of their (power-of-two) size, so a group's fold is exactly a
+// subtree of the global tree.  At every level the pairs are packed into the
+// lowest lanes, so a level with p pairs keeps ceil(p / 64) waves busy rather
+// than touching every wave of the group.
+//
+// Costs on gfx950: a funnel shift (the rotate) and a three-input add issue at
+// half the rate of a plain add, xor or three-input logic op, and one wave
+// alone gets half of its SIMD's issue rate.  The leaves run at about 3.5
+// waves per SIMD for a 235 MB tensor; the top of the tree is a chain of two
+// compressions per level on one lane.
 //
 // Everything is 32-bit integer arithmetic; there is no floating point here.
 #include <hip/hip_runtime.h>
@@ -28,7 +37,8 @@
 namespace repops {
 namespace {
 
-constexpr int kGroup = 256;
+constexpr int kLeafGroup = 256;   // lanes (and leaves) per workgroup, first launch
+constexpr int kNodeGroup = 1024;  // lanes (and digests) per workgroup, later launches
 
 // FIPS 180-4, section 4.2.2: the first 32 bits of the fractional parts of
 // the cube roots of the first 64 primes.
@@ -51,6 +61,16 @@ constexpr uint32_t kInit[8] = {0x6a09e667u, 0xbb67ae85u, 0x3c6ef372u, 0xa54ff53a
 
 __host__ __device__ __forceinline__ uint32_t rotr(uint32_t x, int n) { return (x >> n) | (x << (32 - n)); }
 
+// a ^ b ^ c in one instruction on the device (three-input logic op, truth
+// table 0x96); the host build of these helpers serves host-side checks.
+__host__ __device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+#if __HIP_DEVICE_COMPILE__
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+#else
+    return a ^ b ^ c;
+#endif
+}
+
 __host__ __device__ __forceinline__ uint32_t bswap32(uint32_t x) { return __builtin_bswap32(x); }
 
 __host__ __device__ __forceinline__ void init_state(uint32_t (&h)[8]) {
@@ -69,15 +89,15 @@ __host__ __device__ __forceinline__ void compress(uint32_t (&h)[8], uint32_t (&w
             wt = w[t];
         } else {
             const uint32_t w15 = w[(t - 15) & 15], w2 = w[(t - 2) & 15];
-            const uint32_t s0 = rotr(w15, 7) ^ rotr(w15, 18) ^ (w15 >> 3);
-            const uint32_t s1 = rotr(w2, 17) ^ rotr(w2, 19) ^ (w2 >> 10);
+            const uint32_t s0 = xor3(rotr(w15, 7), rotr(w15, 18), w15 >> 3);
+            const uint32_t s1 = xor3(rotr(w2, 17), rotr(w2, 19), w2 >> 10);
             wt = w[t & 15] + s0 + w[(t - 7) & 15] + s1;
             w[t & 15] = wt;
         }
-        const uint32_t S1 = rotr(e, 6) ^ rotr(e, 11) ^ rotr(e, 25);
+        const uint32_t S1 = xor3(rotr(e, 6), rotr(e, 11), rotr(e, 25));
         const uint32_t ch = (e & f) ^ (~e & g);
         const uint32_t t1 = hh + S1 + ch + kRound[t] + wt;
-        const uint32_t S0 = rotr(a, 2) ^ rotr(a, 13) ^ rotr(a, 22);
+        const uint32_t S0 = xor3(rotr(a, 2), rotr(a, 13), rotr(a, 22));
         const uint32_t maj = (a & b) ^ (a & c) ^ (b & c);
         const uint32_t t2 = S0 + maj;
         hh = g;
@@ -107,6 +127,25 @@ __host__ __device__ __forceinline__ uint32_t shifted_word(uint32_t prev, uint32_
     return (prev & 0xff000000u) | (bswap32(d) >> 8);
 }
 
+// The 16 words at q (VEC: q is 16-byte aligned, four 16-byte loads).
+template <bool VEC>
+__host__ __device__ __forceinline__ void load_block(const uint32_t* __restrict__ q,
+                                                    uint32_t (&d)[16]) {
+    if constexpr (VEC) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const uint4 x = *reinterpret_cast<const uint4*>(q + 4 * v);
+            d[4 * v] = x.x;
+            d[4 * v + 1] = x.y;
+            d[4 * v + 2] = x.z;
+            d[4 * v + 3] = x.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) d[j] = q[j];
+    }
+}
+
 // SHA-256(0x00 || the nw words at p): message length 4*nw + 1 bytes.
 // VEC: p is 16-byte aligned, full blocks are read as four 16-byte loads.
 template <bool VEC>
@@ -115,22 +154,14 @@ __host__ __device__ __forceinline__ void hash_leaf(const uint32_t* __restrict__ 
     init_state(h);
     uint32_t prev = 0;
     const int64_t full = nw >> 4;  // blocks made only of data-derived words
+    // Full blocks, each block's words loaded one block ahead of its use.
+    uint32_t nxt[16];
+    if (full > 0) load_block<VEC>(p, nxt);
     for (int64_t blk = 0; blk < full; ++blk) {
         uint32_t d[16], w[16];
-        const uint32_t* q = p + (blk << 4);
-        if constexpr (VEC) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const uint4 x = *reinterpret_cast<const uint4*>(q + 4 * v);
-                d[4 * v] = x.x;
-                d[4 * v + 1] = x.y;
-                d[4 * v + 2] = x.z;
-                d[4 * v + 3] = x.w;
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) d[j] = q[j];
-        }
+        for (int j = 0; j < 16; ++j) d[j] = nxt[j];
+        if (blk + 1 < full) load_block<VEC>(p + ((blk + 1) << 4), nxt);
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             w[j] = shifted_word(prev, d[j]);
@@ -186,18 +217,21 @@ __host__ __device__ __forceinline__ void hash_node(const uint32_t (&l)[8], const
 
 // One stage.  LEAF: item i is leaf i of the data (words [i*leaf_words,
 // min((i+1)*leaf_words, total_words))); otherwise item i is the digest
-// src[8i .. 8i+7].  Writes one digest per workgroup to dst[8*blockIdx.x ..];
-// FINAL (a single workgroup): the root, as the digest's 32 bytes.
-template <bool LEAF, bool VEC, bool FINAL>
-__global__ __launch_bounds__(kGroup) void repops_merkle_kernel(const uint32_t* __restrict__ src,
-                                                               int64_t n_items, int64_t leaf_words,
-                                                               int64_t total_words,
-                                                               uint32_t* __restrict__ dst) {
-    __shared__ uint32_t node[8][kGroup];
+// src[8i .. 8i+7].  A workgroup of G lanes takes G consecutive items and
+// writes the root of their subtree to dst[8*blockIdx.x ..]; FINAL (a single
+// workgroup): the root of the whole tree, as the digest's 32 bytes.
+template <int G, bool LEAF, bool VEC, bool FINAL>
+__global__ __launch_bounds__(G) void repops_merkle_kernel(const uint32_t* __restrict__ src,
+                                                          int64_t n_items, int64_t leaf_words,
+                                                          int64_t total_words,
+                                                          uint32_t* __restrict__ dst) {
+    // Two node buffers: level l reads one and writes the other, so one
+    // barrier per level separates every write from the reads before it.
+    __shared__ uint32_t node[2][8][G];
     const int tid = static_cast<int>(threadIdx.x);
-    const int64_t first = static_cast<int64_t>(blockIdx.x) * kGroup;
+    const int64_t first = static_cast<int64_t>(blockIdx.x) * G;
     const int64_t rem = n_items - first;
-    const int count = rem < kGroup ? static_cast<int>(rem) : kGroup;
+    const int count = rem < G ? static_cast<int>(rem) : G;
 
     uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (tid < count) {
@@ -211,23 +245,33 @@ __global__ __launch_bounds__(kGroup) void repops_merkle_kernel(const uint32_t* _
             for (int q = 0; q < 8; ++q) h[q] = src[item * 8 + q];
         }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) node[q][tid] = h[q];
+        for (int q = 0; q < 8; ++q) node[0][q][tid] = h[q];
     }
-    // Level by level: the node at lane tid (a multiple of 2*half) takes its
-    // right neighbour at tid + half if there is one, else is carried up.
-    for (int half = 1; half < count; half *= 2) {
+    // Level by level over n nodes held in slots 0..n-1 of one buffer: lane p
+    // hashes the pair (2p, 2p+1) into slot p of the other buffer; with n odd,
+    // lane n/2 carries the last node up unchanged.  Lane 0 ends with the root.
+    int cur = 0;
+    for (int n = count; n > 1; n = (n + 1) >> 1) {
         __syncthreads();
-        if ((tid & (2 * half - 1)) == 0 && tid + half < count) {
-            uint32_t r[8], out[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) r[q] = node[q][tid + half];
-            hash_node(h, r, out);
+        const int pairs = n >> 1;
+        if (tid < pairs) {
+            uint32_t l[8], r[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                h[q] = out[q];
-                node[q][tid] = out[q];
+                l[q] = node[cur][q][2 * tid];
+                r[q] = node[cur][q][2 * tid + 1];
+            }
+            hash_node(l, r, h);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) node[cur ^ 1][q][tid] = h[q];
+        } else if (tid == pairs && (n & 1)) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                h[q] = node[cur][q][n - 1];
+                node[cur ^ 1][q][tid] = h[q];
             }
         }
+        cur ^= 1;
     }
     if (tid == 0) {
         uint32_t* o = dst + static_cast<int64_t>(blockIdx.x) * 8;
@@ -270,11 +314,12 @@ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 }  // namespace
 
 int64_t merkle_workspace_bytes(int64_t n_leaves) {
-    // Two ping-pong buffers: the first stage's digests and the second's; later
-    // stages alternate between them (each is consumed before it is refilled).
-    if (n_leaves <= kGroup) return 0;
-    const int64_t n1 = ceil_div(n_leaves, kGroup);
-    const int64_t n2 = ceil_div(n1, kGroup);
+    // Two ping-pong buffers: the first launch's digests and the second's;
+    // later launches alternate between them (each is consumed before it is
+    // refilled, in stream order).
+    if (n_leaves <= kLeafGroup) return 0;
+    const int64_t n1 = ceil_div(n_leaves, kLeafGroup);
+    const int64_t n2 = ceil_div(n1, kNodeGroup);
     return round_up(n1 * 32, 256) + (n2 > 1 ? round_up(n2 * 32, 256) : 0);
 }
 
@@ -286,7 +331,7 @@ int launch_merkle_root(const uint32_t* data, int64_t total_words, int64_t leaf_w
         return static_cast<int>(hipGetLastError());
     }
     const int64_t n_leaves = ceil_div(total_words, leaf_words);
-    const int64_t n1 = ceil_div(n_leaves, kGroup);
+    const int64_t n1 = ceil_div(n_leaves, kLeafGroup);
     uint32_t* buf[2] = {static_cast<uint32_t*>(ws), nullptr};
     if (n1 > 1) buf[1] = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + round_up(n1 * 32, 256));
 
@@ -294,19 +339,20 @@ int launch_merkle_root(const uint32_t* data, int64_t total_words, int64_t leaf_w
     int64_t n = n_leaves;
     const uint32_t* src = data;
     for (int stage = 0;; ++stage) {
-        const int64_t blocks = ceil_div(n, kGroup);
+        const int group = stage == 0 ? kLeafGroup : kNodeGroup;
+        const int64_t blocks = ceil_div(n, group);
         const bool final_stage = blocks == 1;
         uint32_t* dst = final_stage ? root : buf[stage & 1];
         Fn fn;
         if (stage == 0)
-            fn = final_stage ? (vec ? repops_merkle_kernel<true, true, true>
-                                    : repops_merkle_kernel<true, false, true>)
-                             : (vec ? repops_merkle_kernel<true, true, false>
-                                    : repops_merkle_kernel<true, false, false>);
+            fn = final_stage ? (vec ? repops_merkle_kernel<kLeafGroup, true, true, true>
+                                    : repops_merkle_kernel<kLeafGroup, true, false, true>)
+                             : (vec ? repops_merkle_kernel<kLeafGroup, true, true, false>
+                                    : repops_merkle_kernel<kLeafGroup, true, false, false>);
         else
-            fn = final_stage ? repops_merkle_kernel<false, false, true>
-                             : repops_merkle_kernel<false, false, false>;
-        hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(kGroup), 0, s, src, n,
+            fn = final_stage ? repops_merkle_kernel<kNodeGroup, false, false, true>
+                             : repops_merkle_kernel<kNodeGroup, false, false, false>;
+        hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(group), 0, s, src, n,
                            leaf_words, total_words, dst);
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return static_cast<int>(err);

@@ -218,3 +218,24 @@ def make_batched_operands(name: str):
     a_shape = (w.batch, w.K, w.M) if w.trans_a else (w.batch, w.M, w.K)
     b_shape = (w.batch, w.N, w.K) if w.trans_b else (w.batch, w.K, w.N)
     return _draw(w.a_dist, a_shape, w.seed + 1), _draw(w.b_dist, b_shape, w.seed + 2)
+
+
+@dataclass(frozen=True)
+class HashWorkload:
+    """Hashing one operator output: the tensor hash a trainer attaches to a
+    graph node and the referee recomputes in a dispute.  The hashed tensor
+    is the output C of the named matmul workload."""
+    name: str
+    source: str
+    leaf_bytes: int
+    description: str
+
+
+HASH_WORKLOADS = {
+    w.name: w
+    for w in [
+        HashWorkload("merkle_llama8b_mlp_up_C", "llama8b_mlp_up", 1024,
+                     "SHA-256 Merkle tree hash of the Llama-3.1-8B-shaped up-projection output "
+                     "C (4096 x 14336 float32, 235 MB) in 1 KiB leaves"),
+    ]
+}

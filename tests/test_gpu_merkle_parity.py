@@ -4,7 +4,8 @@ ABI, against the CPU oracle (oracle/merkle.py), byte for byte.
 
 Covered: the empty input; one-block and two-block padding boundaries; a
 tree of exactly one workgroup (256 leaves) and trees needing two and three
-launches; leaf sizes from 4 bytes to 2^24 bytes; the narrow-load path
+launches (the first folds groups of 256 leaves, later ones groups of 1024
+digests); leaf sizes from 4 bytes to 2^24 bytes; the narrow-load path
 (leaves not a multiple of 16 bytes, data only 4-byte aligned); workspace
 reuse across calls; the tensor hash of matmul outputs; the referee's verdicts
 (an honest claim, a claim one bit off, a claim from another summation order,
@@ -65,7 +66,8 @@ CASES = [
     (256 * 1024, 1024, 0),          # 256 leaves: one launch
     (256 * 1024 + 4, 1024, 0),      # 257 leaves: two launches
     (65536 * 4, 4, 0),              # 65536 leaves: two launches
-    (65537 * 4, 4, 0),              # 65537 leaves: three launches
+    (65537 * 4, 4, 0),              # 257 digests after the first launch
+    ((256 * 1024 + 1) * 4, 4, 0),   # 262145 leaves: three launches
     (1000 * 52 + 12, 52, 0),        # leaves not a multiple of 16 bytes
     (300 * 1024 + 8, 1024, 1),      # data 4-byte but not 16-byte aligned
     (77 * 4096 + 2048, 4096, 0),

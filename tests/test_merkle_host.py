@@ -67,7 +67,8 @@ def test_workspace_query():
     assert ws(0, 1024) == 0
     assert ws(256 * 1024, 1024) == 0            # 256 leaves: one workgroup
     assert ws(256 * 1024 + 4, 1024) == 256      # 257 leaves: two digests
-    assert ws(4096 * 14336 * 4, 1024) == 28672 + 256
+    assert ws(4096 * 14336 * 4, 1024) == 28672    # 896 digests, then one group
+    assert ws(4 * (256 * 1024 + 1), 4) == 33024 + 256  # 1025 digests, then 2
     for nbytes, leaf in ((6, 4), (-4, 4), (8, 6), (8, 0), (8, 2), (8, (1 << 24) + 4),
                          ((1 << 50) + 4, 1024)):
         assert ws(nbytes, leaf) == -1, (nbytes, leaf)
