@@ -44,6 +44,7 @@ GCC_FLAGS = [
     "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math",
     "-fexcess-precision=standard", "-fPIC", "-shared", "-pthread",
 ]
+GCC_LIBS = ["-lm"]
 
 _lib = None
 
@@ -53,7 +54,7 @@ def build(force: bool = True) -> str:
     global _lib
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.run(["gcc", *GCC_FLAGS, "-o", tmp, _SRC], check=True)
+        subprocess.run(["gcc", *GCC_FLAGS, "-o", tmp, _SRC, *GCC_LIBS], check=True)
         os.replace(tmp, _LIB)
         _lib = None
     return _LIB
@@ -78,6 +79,13 @@ def _load():
             fp, i64, i64, i64, fp, i64, i64, i64, fp, i64, i64, i64, i64, i64, i64, i64,
             ip, ip, fp, i64, i64, ip]
         lib.repops_oracle_matmul_batched_f32.restype = ip
+        lib.repops_oracle_erf_f32.argtypes = [fp, fp, i64]
+        lib.repops_oracle_erf_f32.restype = ip
+        lib.repops_oracle_gelu_f32.argtypes = [fp, fp, i64]
+        lib.repops_oracle_gelu_f32.restype = ip
+        lib.repops_oracle_layernorm_f32.argtypes = [fp, i64, fp, fp, fp, i64, i64, i64,
+                                                    ctypes.c_float, fp, fp]
+        lib.repops_oracle_layernorm_f32.restype = ip
         lib.repops_oracle_env_status.argtypes = []
         lib.repops_oracle_env_status.restype = ip
         _lib = lib
@@ -225,3 +233,54 @@ def matmul_batched_f32(A: np.ndarray, B: np.ndarray, trans_a: bool = False,
     if rc != 0:
         raise RuntimeError("oracle failed with status %d" % rc)
     return out
+
+
+def _f32_1d(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32)).reshape(-1)
+
+
+def erf_f32(x) -> np.ndarray:
+    """erf by Abramowitz and Stegun 7.1.28 in the fixed binary32 order of
+    repops_oracle.c; same shape as x."""
+    x = np.asarray(x, dtype=np.float32)
+    xf = _f32_1d(x)
+    y = np.empty_like(xf)
+    rc = _load().repops_oracle_erf_f32(xf.ctypes.data, y.ctypes.data, xf.size)
+    if rc != 0:
+        raise RuntimeError("oracle erf failed (%d)" % rc)
+    return y.reshape(x.shape)
+
+
+def gelu_f32(x) -> np.ndarray:
+    """GeLU = (x * 0.5) * (1 + erf(x * RN(1/sqrt 2))) in the fixed binary32 order."""
+    x = np.asarray(x, dtype=np.float32)
+    xf = _f32_1d(x)
+    y = np.empty_like(xf)
+    rc = _load().repops_oracle_gelu_f32(xf.ctypes.data, y.ctypes.data, xf.size)
+    if rc != 0:
+        raise RuntimeError("oracle gelu failed (%d)" % rc)
+    return y.reshape(x.shape)
+
+
+def layernorm_f32(x, gamma=None, beta=None, eps=1e-5):
+    """LayerNorm over the last dimension of a 2-D array, fixed order (see
+    repops_oracle.c).  Returns (y, mean, rstd)."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    if x.ndim != 2:
+        raise ValueError("x must be 2-D (rows, H)")
+    rows, H = x.shape
+    g = None if gamma is None else _f32_1d(gamma)
+    b = None if beta is None else _f32_1d(beta)
+    for v in (g, b):
+        if v is not None and v.size != H:
+            raise ValueError("gamma and beta need H elements")
+    y = np.empty_like(x)
+    mean = np.empty(rows, np.float32)
+    rstd = np.empty(rows, np.float32)
+    rc = _load().repops_oracle_layernorm_f32(
+        x.ctypes.data, H, None if g is None else g.ctypes.data,
+        None if b is None else b.ctypes.data, y.ctypes.data, H, rows, H,
+        float(np.float32(eps)), mean.ctypes.data, rstd.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle layernorm failed (%d)" % rc)
+    return y, mean, rstd

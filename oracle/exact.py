@@ -170,3 +170,158 @@ def exact_matmul_bias(A: np.ndarray, B: np.ndarray, bias: np.ndarray) -> np.ndar
             out[i, j] = encode(exact_add(decode_binary32(int(cbits[i, j])),
                                          decode_binary32(int(bbits[j]))))
     return out.view(np.float32)
+
+
+# ---- ERF, GeLU and LayerNorm by exact arithmetic ---------------------------
+# The same operation sequences as repops_oracle.c, each +, -, *, / and sqrt
+# computed exactly and rounded once to binary32 by round_binary32.  Constants
+# are the decimals of the definitions rounded exactly to binary32 here.
+
+def exact_div(x, y):
+    if x[0] == "nan" or y[0] == "nan":
+        return ("nan", 0, None)
+    s = x[1] ^ y[1]
+    if x[0] == "inf":
+        return ("nan", 0, None) if y[0] == "inf" else ("inf", s, None)
+    if y[0] == "inf":
+        return ("num", s, Fraction(0))
+    if y[2] == 0:
+        return ("nan", 0, None) if x[2] == 0 else ("inf", s, None)
+    return decode_binary32(round_binary32(s, x[2] / y[2]))
+
+
+def _next_up(m: Fraction) -> Fraction:
+    bits = round_binary32(0, m)
+    return decode_binary32(bits + 1)[2]
+
+
+def _next_down(m: Fraction) -> Fraction:
+    bits = round_binary32(0, m)
+    return decode_binary32(bits - 1)[2]
+
+
+def exact_sqrt(x):
+    """Correctly rounded binary32 square root: the representable r whose
+    rounding interval holds sqrt(m), found by comparing squared midpoints
+    exactly (sqrt of a binary32 value is never a midpoint)."""
+    if x[0] == "nan" or (x[1] == 1 and not (x[0] == "num" and x[2] == 0)):
+        return ("nan", 0, None)
+    if x[0] == "inf":
+        return x
+    m = x[2]
+    if m == 0:
+        return x
+    # start from a binary32 near sqrt(m), then walk to the right one
+    guess = Fraction(float(m) ** 0.5)
+    r = decode_binary32(round_binary32(0, guess))[2]
+    while True:
+        lo = (_next_down(r) + r) / 2 if r > 0 else Fraction(0)
+        hi = (r + _next_up(r)) / 2
+        if lo * lo > m:
+            r = _next_down(r)
+        elif hi * hi < m:
+            r = _next_up(r)
+        else:
+            return ("num", 0, r)
+
+
+def _const(dec: str):
+    v = Fraction(dec)
+    return decode_binary32(round_binary32(1 if v < 0 else 0, abs(v)))
+
+
+ERF_SERIES_DEC = ["1.128379167095512573896e+0", "-3.761263890318375246321e-1",
+                  "1.128379167095512573896e-1", "-2.686617064513125175943e-2",
+                  "5.223977625442187842112e-3", "-8.548327023450852832547e-4",
+                  "1.205533298178966425103e-4", "-1.492565035840625097746e-5",
+                  "1.646211436588924740161e-6", "-1.636584469123492431739e-7",
+                  "1.480719281587921723955e-8"]
+AS_7128_DEC = ["0.0705230784", "0.0422820123", "0.0092705272", "0.0001520143",
+               "0.0002765672", "0.0000430638"]
+INV_SQRT2_DEC = "0.70710678118654752440"
+
+ONE = ("num", 0, Fraction(1))
+
+
+def exact_erf(x):
+    """erf in two pieces split at |x| = 1 (Maclaurin series below,
+    Abramowitz and Stegun 7.1.28 at and above, and for NaN)."""
+    if x[0] == "nan":
+        return x
+    y = ("inf", 0, None) if x[0] == "inf" else ("num", 0, x[2])
+    if y[0] == "num" and y[2] < 1:
+        c = [_const(d) for d in ERF_SERIES_DEC]
+        w = exact_mul(x, x)
+        s = c[10]
+        for n in range(9, -1, -1):
+            s = exact_add(exact_mul(s, w), c[n])
+        return exact_mul(s, x)
+    a = [_const(d) for d in AS_7128_DEC]
+    p = a[5]
+    for i in range(4, -1, -1):
+        p = exact_add(exact_mul(p, y), a[i])
+    p = exact_add(exact_mul(p, y), ONE)
+    q = exact_mul(p, p)
+    for _ in range(3):
+        q = exact_mul(q, q)
+    r = exact_div(ONE, q)
+    e = exact_add(ONE, exact_neg(r))
+    return e if e[0] == "nan" else (e[0], x[1], e[2])
+
+
+def exact_gelu(x):
+    """(x * 0.5) * (1 + erf(x * RN(1/sqrt 2)))."""
+    u = exact_mul(x, _const(INV_SQRT2_DEC))
+    e = exact_erf(u)
+    h = exact_mul(x, ("num", 0, Fraction(1, 2)))
+    t = exact_add(ONE, e)
+    return exact_mul(h, t)
+
+
+def exact_unary(fn, x: np.ndarray) -> np.ndarray:
+    bits = np.ascontiguousarray(np.asarray(x, dtype=np.float32)).view(np.uint32)
+    out = np.array([encode(fn(decode_binary32(int(b)))) for b in bits.reshape(-1)],
+                   dtype=np.uint32)
+    return out.view(np.float32).reshape(bits.shape)
+
+
+def exact_layernorm(x: np.ndarray, gamma=None, beta=None, eps=1e-5):
+    """Fixed-order LayerNorm of each row by exact arithmetic: S = +0 + x_0 +
+    ... (ascending), mu = S / H, S2 = sum of (x_i - mu)^2 ascending from +0,
+    var = S2 / H, rstd = 1 / sqrt(var + eps), y = ((x - mu) * rstd) * gamma +
+    beta.  Returns (y, mean, rstd) float32."""
+    X = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    rows, H = X.shape
+    xb = X.view(np.uint32)
+    g = None if gamma is None else [decode_binary32(int(b)) for b in
+                                    np.asarray(gamma, np.float32).view(np.uint32)]
+    bt = None if beta is None else [decode_binary32(int(b)) for b in
+                                    np.asarray(beta, np.float32).view(np.uint32)]
+    ep = decode_binary32(int(np.float32(eps).view(np.uint32)))
+    fh = ("num", 0, Fraction(H))
+    y = np.empty((rows, H), np.uint32)
+    mean = np.empty(rows, np.uint32)
+    rstd = np.empty(rows, np.uint32)
+    for r in range(rows):
+        v = [decode_binary32(int(b)) for b in xb[r]]
+        s = ("num", 0, Fraction(0))
+        for t in v:
+            s = exact_add(s, t)
+        mu = exact_div(s, fh)
+        s2 = ("num", 0, Fraction(0))
+        for t in v:
+            d = exact_add(t, exact_neg(mu))
+            s2 = exact_add(s2, exact_mul(d, d))
+        var = exact_div(s2, fh)
+        sd = exact_sqrt(exact_add(var, ep))
+        rs = exact_div(ONE, sd)
+        for i, t in enumerate(v):
+            o = exact_mul(exact_add(t, exact_neg(mu)), rs)
+            if g is not None:
+                o = exact_mul(o, g[i])
+            if bt is not None:
+                o = exact_add(o, bt[i])
+            y[r, i] = encode(o)
+        mean[r] = encode(mu)
+        rstd[r] = encode(rs)
+    return y.view(np.float32), mean.view(np.float32), rstd.view(np.float32)

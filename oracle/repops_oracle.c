@@ -42,6 +42,7 @@
 #define _GNU_SOURCE
 #include <fenv.h>
 #include <float.h>
+#include <math.h>
 #include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -253,6 +254,145 @@ int repops_oracle_matmul_batched_f32(const float *A, int64_t a_bs, int64_t a_rs,
                     Cb[i * c_rs + j * c_cs] = s + bias[b * bias_bs + j * bias_s];
                 }
         }
+    }
+    return 0;
+}
+
+/* ---- Other RepOps operators: ERF, GeLU, LayerNorm ------------------------
+ * The Verde and RepOps article (section 4.3) names LayerNorm, GeLU and ERF as
+ * the operators behind DistilBERT's higher overhead, without formulas.  Each
+ * function below fixes one sequence of binary32 operations (every +, -, *, /
+ * and sqrt rounded to nearest even on its own, IEEE gradual underflow), so the
+ * result is one bit pattern on any IEEE machine.
+ */
+
+/* erf, in two pieces split at |x| = 1.
+ *
+ * |x| < 1: the Maclaurin series erf x = (2/sqrt pi) sum_n (-1)^n x^(2n+1) /
+ * (n! (2n+1)), truncated after n = 10 (the first omitted term is below
+ * 1.3e-9 there).  Coefficient n is that exact value rounded to binary32 (the
+ * decimals below carry 22 digits of it).  Evaluation: w = x*x; by Horner's
+ * rule in w from c10 down, s = c10; s = s*w + c9; ...; s = s*w + c0; then
+ * erf x = s * x.
+ *
+ * |x| >= 1 (and NaN): Abramowitz and Stegun, Handbook of Mathematical
+ * Functions (1964), formula 7.1.28: for y >= 0,
+ *     erf y = 1 - 1 / (1 + a1 y + a2 y^2 + a3 y^3 + a4 y^4 + a5 y^5 + a6 y^6)^16
+ * with absolute error at most 3e-7 in exact arithmetic; the coefficients are
+ * the handbook's decimals rounded to binary32.  Evaluation: y = |x|; p = a6;
+ * p = p*y + a5; ...; p = p*y + a1; p = p*y + 1; q = p^16 by four squarings;
+ * r = 1/q; e = 1 - r; erf x = e with the sign of x.
+ * (Below |x| = 1 the 16th power would magnify the rounding of p to about
+ * 2e-6; the series keeps the binary32 result within a few units of the last
+ * place there.) */
+static const float ERF_SERIES[11] = {
+    1.128379167095512573896e+0f, -3.761263890318375246321e-1f, 1.128379167095512573896e-1f,
+    -2.686617064513125175943e-2f, 5.223977625442187842112e-3f, -8.548327023450852832547e-4f,
+    1.205533298178966425103e-4f, -1.492565035840625097746e-5f, 1.646211436588924740161e-6f,
+    -1.636584469123492431739e-7f, 1.480719281587921723955e-8f};
+static const float AS_7128[6] = {0.0705230784f, 0.0422820123f, 0.0092705272f,
+                                 0.0001520143f, 0.0002765672f, 0.0000430638f};
+
+static float erf_piecewise(float x)
+{
+    const float y = fabsf(x);
+    if (y < 1.0f) {
+        const float w = x * x;
+        float s = ERF_SERIES[10];
+        for (int n = 9; n >= 0; --n) {
+            s = s * w;
+            s = s + ERF_SERIES[n];
+        }
+        return s * x;
+    }
+    float p = AS_7128[5];
+    for (int i = 4; i >= 0; --i) {
+        p = p * y;
+        p = p + AS_7128[i];
+    }
+    p = p * y;
+    p = p + 1.0f;
+    float q = p * p;
+    q = q * q;
+    q = q * q;
+    q = q * q;
+    const float r = 1.0f / q;
+    const float e = 1.0f - r;
+    return copysignf(e, x);
+}
+
+/* GeLU(x) = x * Phi(x) = (x / 2) * (1 + erf(x / sqrt 2)), evaluated as
+ * u = x * c with c = 1/sqrt(2) rounded to binary32; h = x * 0.5;
+ * t = 1 + erf(u); GeLU = h * t. */
+static float gelu_erf(float x)
+{
+    const float c = 0.70710678118654752440f;
+    const float u = x * c;
+    const float e = erf_piecewise(u);
+    const float h = x * 0.5f;
+    const float t = 1.0f + e;
+    return h * t;
+}
+
+int repops_oracle_erf_f32(const float *x, float *y, int64_t n)
+{
+    if (n < 0) return -1;
+    if (repops_oracle_env_status() != 0) return -2;
+    for (int64_t i = 0; i < n; ++i) y[i] = erf_piecewise(x[i]);
+    return 0;
+}
+
+int repops_oracle_gelu_f32(const float *x, float *y, int64_t n)
+{
+    if (n < 0) return -1;
+    if (repops_oracle_env_status() != 0) return -2;
+    for (int64_t i = 0; i < n; ++i) y[i] = gelu_erf(x[i]);
+    return 0;
+}
+
+/* LayerNorm over each row of H elements (Ba, Kiros and Hinton, "Layer
+ * Normalization", 2016: normalise by the mean and the biased variance of the
+ * row, then scale by gamma and shift by beta).  Fixed order, per row r:
+ *     S  = +0; for i ascending: S = S + x_i           mu  = S / H
+ *     S2 = +0; for i ascending: d = x_i - mu; S2 = S2 + d*d
+ *     var = S2 / H;  sd = sqrt(var + eps);  rstd = 1 / sd
+ *     y_i = ((x_i - mu) * rstd) * gamma_i + beta_i
+ * every operation rounded on its own (H <= 2^24 converts exactly).  gamma
+ * and beta may be NULL (the multiply or the add is then left out).  mean and
+ * rstd, when not NULL, receive mu and rstd per row.  Row r of x starts at
+ * x + r * x_rs, of y at y + r * y_rs. */
+int repops_oracle_layernorm_f32(const float *x, int64_t x_rs, const float *gamma,
+                                const float *beta, float *y, int64_t y_rs, int64_t rows,
+                                int64_t H, float eps, float *mean, float *rstd)
+{
+    if (rows < 0 || H < 1 || H > ((int64_t)1 << 24)) return -1;
+    if (repops_oracle_env_status() != 0) return -2;
+    const float fh = (float)H;
+    for (int64_t r = 0; r < rows; ++r) {
+        const float *xr = x + r * x_rs;
+        float *yr = y + r * y_rs;
+        float s = 0.0f;
+        for (int64_t i = 0; i < H; ++i) s = s + xr[i];
+        const float mu = s / fh;
+        float s2 = 0.0f;
+        for (int64_t i = 0; i < H; ++i) {
+            const float d = xr[i] - mu;
+            const float sq = d * d;
+            s2 = s2 + sq;
+        }
+        const float var = s2 / fh;
+        const float ve = var + eps;
+        const float sd = sqrtf(ve);
+        const float rs = 1.0f / sd;
+        for (int64_t i = 0; i < H; ++i) {
+            const float d = xr[i] - mu;
+            float t = d * rs;
+            if (gamma) t = t * gamma[i];
+            if (beta) t = t + beta[i];
+            yr[i] = t;
+        }
+        if (mean) mean[r] = mu;
+        if (rstd) rstd[r] = rs;
     }
     return 0;
 }
