@@ -144,6 +144,8 @@ def main():
         return bench_batched(args, torch, rp, inputs, dev)
     if args.workload in inputs.HASH_WORKLOADS:
         return bench_merkle(args, torch, rp, inputs, dev)
+    if args.workload in inputs.OPS_WORKLOADS:
+        return bench_ops(args, torch, rp, inputs, dev)
     w = inputs.WORKLOADS[args.workload]
     log("workload %s: %s" % (w.name, w.description))
     A, B = inputs.make_operands(w.name)
@@ -563,6 +565,89 @@ def bench_merkle(args, torch, rp, inputs, dev):
                     "referee_call_ms": round(float(np.median(ref_ms)), 4),
                     "hash_share_of_referee": round(k_avg / float(np.median(ref_ms)), 4),
                     "verdict_honest_vs_zero_claim": verdict},
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_ops(args, torch, rp, inputs, dev):
+    """ERF, GeLU or LayerNorm over a DistilBERT-shaped activation: one step =
+    one C-ABI call on resident data.  value = algorithmic GB/s (x read and y
+    written once, plus gamma and beta for LayerNorm); roofline bound hbm."""
+    import oracle
+    w = inputs.OPS_WORKLOADS[args.workload]
+    log("ops workload %s: %s" % (w.name, w.description))
+    x, g, b = inputs.make_ops_operands(w.name)
+    xt = torch.from_numpy(x).to(dev)
+    yt = torch.empty_like(xt)
+    gt = torch.from_numpy(g).to(dev) if g is not None else None
+    bt = torch.from_numpy(b).to(dev) if b is not None else None
+    stream = torch.cuda.current_stream(dev)
+    n = x.size
+    if w.op == "layernorm":
+        def step():
+            st = rp.repops_layernorm_f32(xt.data_ptr(), w.H, gt.data_ptr(), bt.data_ptr(),
+                                         yt.data_ptr(), w.H, w.rows, w.H, float(np.float32(w.eps)),
+                                         None, None, stream.cuda_stream)
+            if st != rp.REPOPS_OK:
+                raise rp.RepopsError(st, "repops_layernorm_f32")
+    else:
+        fn = rp.repops_erf_f32 if w.op == "erf" else rp.repops_gelu_f32
+
+        def step():
+            st = fn(xt.data_ptr(), yt.data_ptr(), n, stream.cuda_stream)
+            if st != rp.REPOPS_OK:
+                raise rp.RepopsError(st, w.op)
+
+    for _ in range(args.warmup):
+        step()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        starts[s].record(stream)
+        step()
+        ends[s].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [starts[s].elapsed_time(ends[s]) for s in range(args.steps)]
+    log("per-step ms: " + " ".join("%.4f" % t for t in kernel_ms))
+    nbytes = float(w.algorithmic_bytes)
+    ms_per_step = wall * 1e3 / args.steps
+    k_avg = float(np.mean(kernel_ms))
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (k_avg * 1e-3) / 1e9
+
+    # Bit-exactness gate: the whole output against the oracle.
+    got = yt.cpu().numpy()
+    t0 = time.perf_counter()
+    if w.op == "layernorm":
+        want = oracle.layernorm_f32(x, g, b, w.eps)[0]
+    else:
+        want = (oracle.erf_f32 if w.op == "erf" else oracle.gelu_f32)(x)
+    dt = time.perf_counter() - t0
+    if not np.array_equal(got.view(np.uint32), want.view(np.uint32)):
+        print("bench.py: %s output differs from the oracle; no number is reported" % w.op,
+              file=sys.stderr)
+        sys.exit(3)
+    log("bit-exact on all %d outputs" % n)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": "the whole workload (%d x %d), single thread, %.2f s" % (w.rows, w.H, dt)}
+    rec = {
+        "metric": "fixed-order %s, algorithmic GB/s, bit-exact" % w.op,
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "strong", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded numpy PCG64)",
+        "config": {"workload": "%s rows=%d H=%d" % (w.name, w.rows, w.H), "rows": w.rows,
+                   "H": w.H},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu, "bitexact": True,
+        "kernel_ms": {"mean": round(k_avg, 5), "median": round(float(np.median(kernel_ms)), 5),
+                      "min": round(min(kernel_ms), 5), "max": round(max(kernel_ms), 5)},
     }
     print(json.dumps(rec), flush=True)
 

@@ -33,7 +33,10 @@ from ._lib import (  # noqa: F401
     repops_build_manifest,
     repops_canonical_order,
     repops_check_args_f32,
+    repops_erf_f32,
     repops_fold_mean_sgd_f32,
+    repops_gelu_f32,
+    repops_layernorm_f32,
     repops_matmul_batched_f32,
     repops_matmul_f32,
     repops_matmul_f32_ex,
@@ -301,3 +304,81 @@ def referee_matmul(a, b, claims, *, trans_a: bool = False, trans_b: bool = False
     stream.synchronize()
     return (bytes(root.cpu().numpy().tobytes()),
             [bool(v) for v in match.cpu().numpy()[:len(claims)]], out)
+
+
+def _unary(name, fn, x, out, stream):
+    import torch
+
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.float32:
+        raise TypeError("x must be a float32 tensor")
+    if not x.is_cuda:
+        raise ValueError("x must be on a GPU; this library has no CPU path")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor shaped like x")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    with torch.cuda.device(x.device):
+        st = fn(x.data_ptr(), out.data_ptr(), x.numel(), stream.cuda_stream)
+    if st != REPOPS_OK:
+        raise RepopsError(st, name)
+    return out
+
+
+def erf(x, *, out=None, stream=None):
+    """erf of every element of a contiguous float32 CUDA tensor, by the fixed
+    binary32 evaluation of repops_erf_f32 (``out`` may be ``x``)."""
+    return _unary("repops_erf_f32", repops_erf_f32, x, out, stream)
+
+
+def gelu(x, *, out=None, stream=None):
+    """GeLU (erf form) of every element, fixed binary32 evaluation."""
+    return _unary("repops_gelu_f32", repops_gelu_f32, x, out, stream)
+
+
+def layernorm(x, gamma=None, beta=None, eps: float = 1e-5, *, out=None, return_stats=False,
+              stream=None):
+    """LayerNorm over the last dimension of a float32 CUDA tensor whose rows
+    are contiguous (any leading shape), fixed-order sums.  Returns y, or
+    (y, mean, rstd) with ``return_stats``."""
+    import numpy as np
+    import torch
+
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.float32 or x.dim() < 1:
+        raise TypeError("x must be a float32 tensor")
+    if not x.is_cuda:
+        raise ValueError("x must be on a GPU; this library has no CPU path")
+    H = x.shape[-1]
+    x2 = x.reshape(-1, H) if x.dim() != 2 else x
+    if x2.numel() and x2.stride(1) != 1:
+        raise ValueError("the rows of x must be contiguous")
+    rows = x2.shape[0]
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    y2 = out.view(-1, H) if out.dim() != 2 else out  # a view: never a copy
+    if tuple(out.shape) != tuple(x.shape) or (y2.numel() and y2.stride(1) != 1):
+        raise ValueError("out must be shaped like x with contiguous rows")
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_cuda or t.numel() != H
+                              or not t.is_contiguous()):
+            raise ValueError("%s must be a contiguous float32 CUDA tensor of %d elements"
+                             % (name, H))
+    mean = torch.empty(rows, dtype=torch.float32, device=x.device) if return_stats else None
+    rstd = torch.empty(rows, dtype=torch.float32, device=x.device) if return_stats else None
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    with torch.cuda.device(x.device):
+        st = repops_layernorm_f32(x2.data_ptr(), x2.stride(0) if rows > 1 else H,
+                                  gamma.data_ptr() if gamma is not None else None,
+                                  beta.data_ptr() if beta is not None else None,
+                                  y2.data_ptr(), y2.stride(0) if rows > 1 else H, rows, H,
+                                  float(np.float32(eps)),
+                                  mean.data_ptr() if mean is not None else None,
+                                  rstd.data_ptr() if rstd is not None else None,
+                                  stream.cuda_stream)
+    if st != REPOPS_OK:
+        raise RepopsError(st, "repops_layernorm_f32")
+    return (out, mean, rstd) if return_stats else out

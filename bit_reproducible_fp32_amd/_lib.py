@@ -40,6 +40,9 @@ EXPORTS = (
     "repops_merkle_workspace_bytes",
     "repops_merkle_root",
     "repops_referee_matmul_f32",
+    "repops_erf_f32",
+    "repops_gelu_f32",
+    "repops_layernorm_f32",
 )
 
 _lib = None
@@ -94,6 +97,12 @@ def load():
     lib.repops_referee_matmul_f32.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i64, i64, ci,
                                               ci, i64, vp, i64, vp, i64, vp, vp, vp]
     lib.repops_referee_matmul_f32.restype = ci
+    for name in ("repops_erf_f32", "repops_gelu_f32"):
+        getattr(lib, name).argtypes = [vp, vp, i64, vp]
+        getattr(lib, name).restype = ci
+    lib.repops_layernorm_f32.argtypes = [vp, i64, vp, vp, vp, i64, i64, i64, ctypes.c_float, vp,
+                                         vp, vp]
+    lib.repops_layernorm_f32.restype = ci
     _lib = lib
     return lib
 
@@ -184,6 +193,19 @@ def repops_referee_matmul_f32(A, a_rs, a_cs, B, b_rs, b_cs, C, M, N, K, trans_a,
                                             int(trans_a), int(trans_b), int(leaf_bytes),
                                             workspace, int(workspace_bytes), claims, int(nclaims),
                                             root, match, stream)
+
+
+def repops_erf_f32(x, y, n, stream) -> int:
+    return load().repops_erf_f32(x, y, int(n), stream)
+
+
+def repops_gelu_f32(x, y, n, stream) -> int:
+    return load().repops_gelu_f32(x, y, int(n), stream)
+
+
+def repops_layernorm_f32(x, x_rs, gamma, beta, y, y_rs, rows, H, eps, mean, rstd, stream) -> int:
+    return load().repops_layernorm_f32(x, int(x_rs), gamma, beta, y, int(y_rs), int(rows), int(H),
+                                       float(eps), mean, rstd, stream)
 
 
 strerror = repops_strerror

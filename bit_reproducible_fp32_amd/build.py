@@ -7,6 +7,8 @@ Flags that matter for the arithmetic:
   also carry ``#pragma clang fp contract(off)``);
 * ``-fno-fast-math`` and ``-fno-gpu-flush-denormals-to-zero``: IEEE binary32
   with gradual underflow (kernel descriptors must say denorm mode 3);
+* ``-fhip-fp32-correctly-rounded-divide-sqrt``: binary32 ``/`` and ``sqrt``
+  are the correctly rounded IEEE operations;
 * ``-Xclang -target-feature -Xclang -packed-fp32-ops``: the compiler must not
   form packed two-lane FP32 instructions.
 """
@@ -25,12 +27,14 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 KERNEL_SOURCES = [os.path.join(CSRC, "repops_kernels.hip"), os.path.join(CSRC, "repops_fold.hip"),
-                  os.path.join(CSRC, "repops_merkle.hip")]
+                  os.path.join(CSRC, "repops_merkle.hip"), os.path.join(CSRC, "repops_ops.hip")]
 SOURCES = KERNEL_SOURCES + [os.path.join(CSRC, "repops_api.cpp"),
                             os.path.join(CSRC, "repops_fold_api.cpp"),
-                            os.path.join(CSRC, "repops_merkle_api.cpp")]
+                            os.path.join(CSRC, "repops_merkle_api.cpp"),
+                            os.path.join(CSRC, "repops_ops_api.cpp")]
 
-FP_FLAGS = ["-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero"]
+FP_FLAGS = ["-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
+            "-fhip-fp32-correctly-rounded-divide-sqrt"]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                 # matrix-instruction results land in ordinary VGPRs, where the
                 # VALU adds read them (no accumulation-register copies)

@@ -117,4 +117,12 @@ int launch_merkle_root(const uint32_t* data, int64_t total_words, int64_t leaf_w
 int launch_merkle_match(const uint32_t* root, const uint32_t* claims, int64_t nclaims,
                         int32_t* match, void* stream);
 
+// ERF (op 0) and GeLU (op 1) over n floats; LayerNorm over rows of H
+// (repops_ops.hip).  vec: every pointer 16-byte aligned (and, for LayerNorm,
+// the row strides and H multiples of 4).
+int launch_unary(int op, const float* x, float* y, int64_t n, bool vec, void* stream);
+int launch_layernorm(const float* x, int64_t x_rs, const float* gamma, const float* beta, float* y,
+                     int64_t y_rs, int64_t rows, int64_t H, float eps, float* mean, float* rstd,
+                     bool vec, void* stream);
+
 }  // namespace repops

@@ -239,3 +239,54 @@ HASH_WORKLOADS = {
                      "C (4096 x 14336 float32, 235 MB) in 1 KiB leaves"),
     ]
 }
+
+
+@dataclass(frozen=True)
+class OpsWorkload:
+    """An elementwise (erf, gelu) or row-wise (layernorm) operator over a
+    DistilBERT-shaped activation: batch 32 x sequence 512 tokens, hidden 768,
+    feed-forward 3072, LayerNorm epsilon 1e-12 (the model the Verde and RepOps
+    article measures in section 4.3; synthetic data, no weights)."""
+    name: str
+    op: str
+    rows: int
+    H: int
+    seed: int
+    eps: float
+    description: str
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """x read and y written once; LayerNorm also reads gamma and beta."""
+        n = self.rows * self.H
+        return 8 * n + (8 * self.H if self.op == "layernorm" else 0)
+
+
+OPS_WORKLOADS = {
+    w.name: w
+    for w in [
+        OpsWorkload("distilbert_gelu", "gelu", 32 * 512, 3072, 8001, 0.0,
+                    "GeLU over a DistilBERT feed-forward activation, 16384 tokens x 3072, "
+                    "x ~ N(0,1)"),
+        OpsWorkload("distilbert_erf", "erf", 32 * 512, 3072, 8101, 0.0,
+                    "erf over 16384 x 3072 values ~ N(0, 1/2) (the GeLU argument x/sqrt 2)"),
+        OpsWorkload("distilbert_layernorm", "layernorm", 32 * 512, 768, 8201, 1e-12,
+                    "LayerNorm over DistilBERT hidden states, 16384 tokens x 768, x ~ N(0,1) "
+                    "times 4 plus 0.5, gamma ~ 1 + N(0, 0.02), beta ~ N(0, 0.02), eps 1e-12"),
+    ]
+}
+
+
+def make_ops_operands(name: str):
+    """(x, gamma, beta): x of shape (rows, H); gamma and beta (H,) for
+    LayerNorm, else None."""
+    w = OPS_WORKLOADS[name]
+    if w.op == "erf":
+        x = (_draw("normal1", (w.rows, w.H), w.seed) * np.float32(0.70710678)).astype(np.float32)
+        return x, None, None
+    if w.op == "gelu":
+        return _draw("normal1", (w.rows, w.H), w.seed), None, None
+    x = (_draw("normal1", (w.rows, w.H), w.seed) * np.float32(4) + np.float32(0.5))
+    gamma = (np.float32(1) + _draw("normal0.02", (w.H,), w.seed + 1)).astype(np.float32)
+    beta = _draw("normal0.02", (w.H,), w.seed + 2)
+    return x.astype(np.float32), gamma, beta

@@ -273,6 +273,62 @@ repops_status repops_referee_matmul_f32(const float* A, int64_t a_rs, int64_t a_
                                         const void* claims, int64_t nclaims, void* root,
                                         int32_t* match, void* stream);
 
+/* ---- Other RepOps operators: ERF, GeLU, LayerNorm ------------------------
+ *
+ * The Verde and RepOps article (section 4.3) names LayerNorm, GeLU and ERF as
+ * RepOps operators without giving formulas.  Each call below evaluates one
+ * fixed sequence of binary32 operations, every +, -, *, / and square root
+ * rounded to nearest even on its own (gradual underflow, no fused
+ * multiply-add; division and square root are the correctly rounded IEEE
+ * operations), so every output has one bit pattern on any IEEE machine.
+ */
+
+/*
+ * y[i] = erf(x[i]) for i < n, evaluated in two pieces split at |x| = 1:
+ *   |x| < 1:  s = Horner's rule in w = x*x over c10 .. c0, c_n the binary32
+ *             value of (2/sqrt pi) (-1)^n / (n! (2n+1)) (the Maclaurin series);
+ *             erf = s * x.
+ *   |x| >= 1 and NaN: Abramowitz and Stegun, Handbook of Mathematical
+ *             Functions, 7.1.28: y = |x|; p = Horner's rule over a6 .. a1, 1
+ *             in y; q = p^16 by four squarings; erf = sign(x) * (1 - 1/q).
+ * Error against the true erf: at most 3 units in the last place below 1,
+ * 4.7e-7 absolute above.  erf(+-0) = +-0, erf(+-inf) = +-1.
+ * x, y: device, n floats (y may equal x; other overlaps are rejected).
+ * Errors: REPOPS_ERR_DIM (n < 0 or above 2^46), REPOPS_ERR_NULL,
+ * REPOPS_ERR_ALIAS, REPOPS_ERR_HIP.  n == 0 is a successful no-op.
+ */
+repops_status repops_erf_f32(const float* x, float* y, int64_t n, void* stream);
+
+/*
+ * y[i] = GeLU(x[i]) = (x * 0.5) * (1 + erf(x * c)) with c = 1/sqrt(2) rounded
+ * to binary32 and erf as in repops_erf_f32, left to right.  Error against
+ * x * Phi(x): at most 3.5e-7 * max(1, |x|).  GeLU(-inf) is NaN (-inf * 0).
+ * Arguments and errors as in repops_erf_f32.
+ */
+repops_status repops_gelu_f32(const float* x, float* y, int64_t n, void* stream);
+
+/*
+ * LayerNorm of each of `rows` rows of H floats (Ba, Kiros and Hinton,
+ * "Layer Normalization", 2016), per row:
+ *     S  = +0; for i ascending: S = S + x_i;            mu = S / H
+ *     S2 = +0; for i ascending: d = x_i - mu; S2 = S2 + d * d
+ *     var = S2 / H;  rstd = 1 / sqrt(var + eps)
+ *     y_i = ((x_i - mu) * rstd) * gamma_i + beta_i
+ * Row r of x starts at x + r * x_rs, of y at y + r * y_rs (strides in
+ * elements).  gamma, beta: H floats each, or NULL to leave out the multiply
+ * or the add.  mean, rstd: `rows` floats each receiving mu and rstd, or NULL.
+ * All device memory, borrowed until the queued work completes.  y may equal x
+ * with y_rs == x_rs (in place); no other overlaps between x, y, gamma, beta,
+ * mean and rstd are allowed.
+ * Errors: REPOPS_ERR_DIM (rows < 0, H < 1 or above 2^24, offsets above 2^46
+ * elements), REPOPS_ERR_STRIDE (x_rs < 0, y_rs < 0, or y_rs < H with more
+ * than one row), REPOPS_ERR_NULL (x or y NULL with rows > 0),
+ * REPOPS_ERR_ALIAS, REPOPS_ERR_HIP.  rows == 0 is a successful no-op.
+ */
+repops_status repops_layernorm_f32(const float* x, int64_t x_rs, const float* gamma,
+                                   const float* beta, float* y, int64_t y_rs, int64_t rows,
+                                   int64_t H, float eps, float* mean, float* rstd, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

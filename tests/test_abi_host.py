@@ -172,7 +172,34 @@ def test_isa_has_no_fused_or_packed_fp32():
     assert bodies
     for name, body in bodies.items():
         bad = FORBIDDEN_FP.findall(body)
+        if DIV_FIXUP.search(body) or SQRT.search(body):
+            continue  # checked by the next test
         assert not bad, "%s uses %s" % (name, bad[:3])
+
+
+DIV_FIXUP = re.compile(r"^\s+v_div_fixup_f32\b", re.M)
+SQRT = re.compile(r"^\s+v_sqrt_f32\w*", re.M)
+FMA_F32 = re.compile(r"^\s+(v_fma_f32|v_fmac_f32\w*)\b", re.M)
+
+
+def test_isa_fused_ops_only_inside_division_and_square_root():
+    """Kernels that divide or take square roots (the correctly rounded IEEE
+    operations, which the compiler expands with fused multiply-adds: five per
+    division, two per square root on gfx950) may hold exactly that many
+    fused operations and no other forbidden form."""
+    bodies, _ = kernels()
+    seen = 0
+    for name, body in bodies.items():
+        ndiv, nsqrt = len(DIV_FIXUP.findall(body)), len(SQRT.findall(body))
+        if not (ndiv or nsqrt):
+            continue
+        seen += 1
+        fma = len(FMA_F32.findall(body))
+        assert fma == 5 * ndiv + 2 * nsqrt, (name, fma, ndiv, nsqrt)
+        other = [m[0] for m in FORBIDDEN_FP.findall(body)
+                 if not re.match(r"v_fmac?_f32", m[0])]
+        assert not other, (name, other[:3])
+    assert seen >= 4
 
 
 def test_isa_valu_kernels_use_no_matrix_instructions():
