@@ -132,10 +132,44 @@ __device__ __forceinline__ void store4(float* p, f32x4 v) {
     }
 }
 
+// Rows are walked in blocks of 16 floats in ascending order.  One lane owns
+// a row and there are only as many lanes as rows, so the latency of each
+// lane's loads is hidden by keeping several blocks of its row in flight: a
+// ring of blocks in registers, each refilled as soon as it has been used.
+constexpr int kRing = 8;      // blocks in flight in the two summing passes
+constexpr int kRingOut = 4;   // blocks (of x, gamma and beta) in the output pass
+
+template <bool VEC>
+__device__ __forceinline__ void load_block(const float* p, f32x4 (&b)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) b[q] = load4<VEC>(p + 4 * q);
+}
+
+// f(v) for every float4 v of the first 16*nblk floats of row xr, in order.
+template <bool VEC, typename F>
+__device__ __forceinline__ void walk_row(const float* xr, int64_t nblk, F&& f) {
+    f32x4 ring[kRing][4];
+#pragma unroll
+    for (int j = 0; j < kRing; ++j)
+        if (j < nblk) load_block<VEC>(xr + 16 * j, ring[j]);
+    for (int64_t base = 0; base < nblk; base += kRing) {
+#pragma unroll
+        for (int j = 0; j < kRing; ++j) {
+            const int64_t blk = base + j;
+            if (blk < nblk) {
+                f32x4 cur[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) cur[q] = ring[j][q];
+                if (blk + kRing < nblk) load_block<VEC>(xr + 16 * (blk + kRing), ring[j]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) f(cur[q]);
+            }
+        }
+    }
+}
+
 // One lane per row (the sums over a row are the fixed-order dimension; rows
-// are free).  A row is walked in chunks of 4 elements in ascending order, the
-// next chunk loaded before the current one is used; a tail of H % 4 single
-// elements follows.  VEC: x, y, gamma, beta 16-byte aligned and x_rs, y_rs, H
+// are free).  VEC: x, y, gamma, beta 16-byte aligned and x_rs, y_rs, H
 // multiples of 4.  y may be x itself with y_rs == x_rs: a lane rewrites only
 // its own row, after its last read of each element.
 template <bool VEC>
@@ -147,59 +181,74 @@ __global__ __launch_bounds__(64) void repops_layernorm_kernel(
     if (r >= rows) return;
     const float* xr = x + r * x_rs;
     float* yr = y + r * y_rs;
-    const int64_t H4 = H & ~int64_t(3);
+    const int64_t nblk = H >> 4;
+    const int64_t tail = nblk << 4;
     const float fh = static_cast<float>(H);
 
     // pass 1: S = ((+0 + x_0) + x_1) + ...
     float s = 0.0f;
-    {
-        f32x4 nxt = H4 > 0 ? load4<VEC>(xr) : f32x4{0, 0, 0, 0};
-        for (int64_t i = 0; i < H4; i += 4) {
-            const f32x4 v = nxt;
-            if (i + 4 < H4) nxt = load4<VEC>(xr + i + 4);
-            s = s + v.x;
-            s = s + v.y;
-            s = s + v.z;
-            s = s + v.w;
-        }
-        for (int64_t i = H4; i < H; ++i) s = s + xr[i];
-    }
+    walk_row<VEC>(xr, nblk, [&](f32x4 v) {
+        s = s + v.x;
+        s = s + v.y;
+        s = s + v.z;
+        s = s + v.w;
+    });
+    for (int64_t i = tail; i < H; ++i) s = s + xr[i];
     const float mu = s / fh;
 
     // pass 2: S2 = sum of (x_i - mu)^2 in the same order
     float s2 = 0.0f;
-    {
-        f32x4 nxt = H4 > 0 ? load4<VEC>(xr) : f32x4{0, 0, 0, 0};
-        for (int64_t i = 0; i < H4; i += 4) {
-            const f32x4 v = nxt;
-            if (i + 4 < H4) nxt = load4<VEC>(xr + i + 4);
-            const f32x4 d = v - mu;
-            const f32x4 sq = d * d;
-            s2 = s2 + sq.x;
-            s2 = s2 + sq.y;
-            s2 = s2 + sq.z;
-            s2 = s2 + sq.w;
-        }
-        for (int64_t i = H4; i < H; ++i) {
-            const float d = xr[i] - mu;
-            const float sq = d * d;
-            s2 = s2 + sq;
-        }
+    walk_row<VEC>(xr, nblk, [&](f32x4 v) {
+        const f32x4 d = v - mu;
+        const f32x4 sq = d * d;
+        s2 = s2 + sq.x;
+        s2 = s2 + sq.y;
+        s2 = s2 + sq.z;
+        s2 = s2 + sq.w;
+    });
+    for (int64_t i = tail; i < H; ++i) {
+        const float d = xr[i] - mu;
+        const float sq = d * d;
+        s2 = s2 + sq;
     }
     const float var = s2 / fh;
     const float ve = var + eps;
     const float sd = __builtin_sqrtf(ve);
     const float rs = 1.0f / sd;
 
-    // pass 3: y_i = ((x_i - mu) * rstd) * gamma_i + beta_i
-    for (int64_t i = 0; i < H4; i += 4) {
-        const f32x4 d = load4<VEC>(xr + i) - mu;
-        f32x4 t = d * rs;
-        if (gamma) t = t * load4<VEC>(gamma + i);
-        if (beta) t = t + load4<VEC>(beta + i);
-        store4<VEC>(yr + i, t);
+    // pass 3: y_i = ((x_i - mu) * rstd) * gamma_i + beta_i, with blocks of x,
+    // gamma and beta in flight.
+    {
+        f32x4 rx[kRingOut][4], rg[kRingOut][4], rb[kRingOut][4];
+        auto fill = [&](int j, int64_t blk) {
+            load_block<VEC>(xr + 16 * blk, rx[j]);
+            if (gamma) load_block<VEC>(gamma + 16 * blk, rg[j]);
+            if (beta) load_block<VEC>(beta + 16 * blk, rb[j]);
+        };
+#pragma unroll
+        for (int j = 0; j < kRingOut; ++j)
+            if (j < nblk) fill(j, j);
+        for (int64_t base = 0; base < nblk; base += kRingOut) {
+#pragma unroll
+            for (int j = 0; j < kRingOut; ++j) {
+                const int64_t blk = base + j;
+                if (blk < nblk) {
+                    f32x4 t[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x4 d = rx[j][q] - mu;
+                        t[q] = d * rs;
+                        if (gamma) t[q] = t[q] * rg[j][q];
+                        if (beta) t[q] = t[q] + rb[j][q];
+                    }
+                    if (blk + kRingOut < nblk) fill(j, blk + kRingOut);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) store4<VEC>(yr + 16 * blk + 4 * q, t[q]);
+                }
+            }
+        }
     }
-    for (int64_t i = H4; i < H; ++i) {
+    for (int64_t i = tail; i < H; ++i) {
         const float d = xr[i] - mu;
         float t = d * rs;
         if (gamma) t = t * gamma[i];
