@@ -1,15 +1,18 @@
 #!/usr/bin/env python3
-"""Benchmark of the reproducible fixed-order FP32 matmul on one MI355X.
+"""Benchmark of the reproducible fixed-order FP32 operators on one MI355X.
 
-One step = one call of the C ABI entry point (host dispatch, operand staging,
-fixed-order accumulation, epilogue) on the Llama-3.1-8B-shaped MLP
-up-projection, M=4096 tokens, K=4096, N=14336, with synthetic operands
-(X ~ N(0,1), W ~ N(0,0.02)) already resident in HBM.  Prints ONE JSON line on
-stdout; progress goes to stderr.
+By default one step = one call of the matmul's C ABI entry point (host
+dispatch, operand staging, fixed-order accumulation, epilogue) on the
+Llama-3.1-8B-shaped MLP up-projection, M=4096 tokens, K=4096, N=14336, with
+synthetic operands (X ~ N(0,1), W ~ N(0,0.02)) already resident in HBM.
+``--workload`` selects another matmul shape, a batched (attention-shaped)
+product, the gradient fold, the tensor hash or ERF/GeLU/LayerNorm.  Prints ONE
+JSON line on stdout; progress goes to stderr.
 
 * ``value``: TFLOP/s = 2*M*N*K / (timed wall time / steps).
-* ``roofline``: the dominant (only) kernel's TFLOP/s from HIP events recorded
-  on the launch stream around every timed launch, against the unfused FP32
+* ``roofline``: the dominant (only) kernel's TFLOP/s from one pair of HIP
+  events recorded on the launch stream around the timed steps (the kernels'
+  average duration), against the unfused FP32
   roofline of 78.6 TFLOP/s (256 CUs x 2.4 GHz x 128 FP32 lane operations per
   clock, each separately rounded multiply or add counting one flop).  ``traffic`` comes from the committed
   rocprofv3 FETCH_SIZE/WRITE_SIZE summary when it was taken on the current
@@ -65,6 +68,23 @@ def committed_traffic(variant_name):
         return float(fields["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def timed_region(torch, stream, step, steps):
+    """Run `steps` steps back to back between one pair of HIP events on the
+    launch stream.  Returns (host wall seconds, event milliseconds per step):
+    the kernels' average duration, with no per-step event records in
+    between to inflate short kernels."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, e0.elapsed_time(e1) / steps
 
 
 def cpu_threads():
@@ -173,17 +193,7 @@ def main():
     for _ in range(args.warmup):
         step()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        starts[s].record(stream)
-        step()
-        ends[s].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = [starts[s].elapsed_time(ends[s]) for s in range(args.steps)]
+    wall, k_avg = timed_region(torch, stream, step, args.steps)
 
     # Bit-exactness gate on sampled outputs of the last timed run (the oracle
     # decides); a mismatch reports no number.
@@ -200,11 +210,9 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     flops = float(w.flops)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    k_avg_ms = float(np.mean(kernel_ms))
-    log("per-step kernel ms: " + " ".join("%.3f" % t for t in kernel_ms))
+    k_avg_ms = k_avg
     achieved = flops / (k_avg_ms * 1e-3) / 1e12
-    log("wall %.3f ms/step, kernel avg %.3f ms (min %.3f, max %.3f): %.2f TFLOP/s"
-        % (ms_per_step, k_avg_ms, min(kernel_ms), max(kernel_ms), achieved))
+    log("wall %.3f ms/step, kernel avg %.3f ms: %.2f TFLOP/s" % (ms_per_step, k_avg_ms, achieved))
     h = hashlib.sha256(out.cpu().numpy().tobytes()).hexdigest()
 
     extra = {}
@@ -271,8 +279,7 @@ def main():
         "cpu_baseline": cpu,
         "bitexact_sampled": bitexact,
         "sha256_C": h,
-        "kernel_ms": {"mean": round(k_avg_ms, 4), "median": round(float(np.median(kernel_ms)), 4),
-                      "min": round(min(kernel_ms), 4), "max": round(max(kernel_ms), 4)},
+        "kernel_ms": {"mean": round(k_avg_ms, 4)},
     }
     rec.update(extra)
     print(json.dumps(rec), flush=True)
@@ -297,18 +304,7 @@ def bench_batched(args, torch, rp, inputs, dev):
 
     for _ in range(args.warmup):
         step()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        starts[s].record(stream)
-        step()
-        ends[s].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = [starts[s].elapsed_time(ends[s]) for s in range(args.steps)]
-    log("per-step kernel ms: " + " ".join("%.4f" % t for t in kernel_ms))
+    wall, k_avg = timed_region(torch, stream, step, args.steps)
     C = out.cpu().numpy()
     for h in range(0, w.batch, 5):
         ii, jj = inputs.sample_entries(w.M, w.N, 64, 77 + h)
@@ -320,7 +316,6 @@ def bench_batched(args, torch, rp, inputs, dev):
     log("bit-exact on sampled outputs of every fifth head")
     flops = float(w.flops)
     ms_per_step = wall * 1e3 / args.steps
-    k_avg = float(np.mean(kernel_ms))
     achieved = flops / (k_avg * 1e-3) / 1e12
     cpu = None
     if not args.no_cpu_baseline:
@@ -343,8 +338,7 @@ def bench_batched(args, torch, rp, inputs, dev):
                      "unit": "TFLOP/s", "frac": round(achieved / UNFUSED_PEAK_TFLOPS, 4),
                      "traffic": None},
         "cpu_baseline": cpu, "bitexact_sampled": True,
-        "kernel_ms": {"mean": round(k_avg, 4), "median": round(float(np.median(kernel_ms)), 4),
-                      "min": round(min(kernel_ms), 4), "max": round(max(kernel_ms), 4)},
+        "kernel_ms": {"mean": round(k_avg, 4)},
     }
     print(json.dumps(rec), flush=True)
 
@@ -373,22 +367,10 @@ def bench_fold(args, torch, rp, inputs, dev):
 
     for _ in range(args.warmup):
         step()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        starts[s].record(stream)
-        step()
-        ends[s].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = [starts[s].elapsed_time(ends[s]) for s in range(args.steps)]
-    log("per-step kernel ms: " + " ".join("%.4f" % t for t in kernel_ms))
+    wall, k_avg = timed_region(torch, stream, step, args.steps)
     nbytes = float(w.algorithmic_bytes)
     ms_per_step = wall * 1e3 / args.steps
     value = nbytes / (ms_per_step * 1e-3) / 1e9
-    k_avg = float(np.mean(kernel_ms))
     achieved = nbytes / (k_avg * 1e-3) / 1e9
 
     # Bit-exactness gate: one step from the initial theta, sampled parameters.
@@ -429,8 +411,7 @@ def bench_fold(args, torch, rp, inputs, dev):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
         "cpu_baseline": cpu, "bitexact_sampled": True,
-        "kernel_ms": {"mean": round(k_avg, 5), "median": round(float(np.median(kernel_ms)), 5),
-                      "min": round(min(kernel_ms), 5), "max": round(max(kernel_ms), 5)},
+        "kernel_ms": {"mean": round(k_avg, 5)},
     }
     print(json.dumps(rec), flush=True)
 
@@ -489,20 +470,8 @@ def bench_merkle(args, torch, rp, inputs, dev):
 
     for _ in range(args.warmup):
         step()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        starts[s].record(stream)
-        step()
-        ends[s].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = [starts[s].elapsed_time(ends[s]) for s in range(args.steps)]
-    log("per-step ms: " + " ".join("%.4f" % t for t in kernel_ms))
+    wall, k_avg = timed_region(torch, stream, step, args.steps)
     ms_per_step = wall * 1e3 / args.steps
-    k_avg = float(np.mean(kernel_ms))
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     comp = merkle_compressions(nbytes, w.leaf_bytes)
     achieved = comp * SHA256_MIN_SLOTS / (k_avg * 1e-3) / 1e12
@@ -559,8 +528,7 @@ def bench_merkle(args, torch, rp, inputs, dev):
                      "unit": "T VALU issue slots/s", "frac": round(achieved / VALU_PEAK_TSLOTS, 4),
                      "traffic": None},
         "cpu_baseline": cpu, "bitexact": True,
-        "kernel_ms": {"mean": round(k_avg, 5), "median": round(float(np.median(kernel_ms)), 5),
-                      "min": round(min(kernel_ms), 5), "max": round(max(kernel_ms), 5)},
+        "kernel_ms": {"mean": round(k_avg, 5)},
         "referee": {"matmul_ms": round(float(np.median(mm_ms)), 4),
                     "referee_call_ms": round(float(np.median(ref_ms)), 4),
                     "hash_share_of_referee": round(k_avg / float(np.median(ref_ms)), 4),
@@ -600,21 +568,9 @@ def bench_ops(args, torch, rp, inputs, dev):
 
     for _ in range(args.warmup):
         step()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        starts[s].record(stream)
-        step()
-        ends[s].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = [starts[s].elapsed_time(ends[s]) for s in range(args.steps)]
-    log("per-step ms: " + " ".join("%.4f" % t for t in kernel_ms))
+    wall, k_avg = timed_region(torch, stream, step, args.steps)
     nbytes = float(w.algorithmic_bytes)
     ms_per_step = wall * 1e3 / args.steps
-    k_avg = float(np.mean(kernel_ms))
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (k_avg * 1e-3) / 1e9
 
@@ -646,8 +602,7 @@ def bench_ops(args, torch, rp, inputs, dev):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
         "cpu_baseline": cpu, "bitexact": True,
-        "kernel_ms": {"mean": round(k_avg, 5), "median": round(float(np.median(kernel_ms)), 5),
-                      "min": round(min(kernel_ms), 5), "max": round(max(kernel_ms), 5)},
+        "kernel_ms": {"mean": round(k_avg, 5)},
     }
     print(json.dumps(rec), flush=True)
 

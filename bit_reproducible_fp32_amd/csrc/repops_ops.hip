@@ -105,158 +105,269 @@ __global__ __launch_bounds__(256) void repops_unary_kernel(const float* x, float
     for (int64_t e = from + t0; e < n; e += stride) y[e] = unary<OP>(x[e]);
 }
 
-// Four consecutive floats of a row (VEC: one 16-byte load).
+// LayerNorm.  The two sums over a row are the fixed-order dimension, so one
+// lane owns a row and walks it in ascending order; rows are the free
+// dimension.  To keep the loads coalesced, a workgroup of kLnThreads lanes owns
+// kLnRows consecutive rows and streams them through LDS in tiles of kLnRows x
+// kLnCols: every lane helps load a tile (consecutive lanes read consecutive
+// floats of a row), then lane r consumes row r of the tile.  Tiles are loaded
+// kLnDepth ahead into registers and double-buffered in LDS.  The output pass
+// has no order to keep, so all lanes stream it directly.
+constexpr int kLnRows = 16;
+constexpr int kLnCols = 64;
+constexpr int kLnThreads = 64;
+constexpr int kLnPitch = kLnCols + 4;            // 16-byte rows, staggered banks
+constexpr int kLnPerThread = kLnRows * kLnCols / kLnThreads;
+constexpr int kLnDepth = 4;                      // tiles in flight per workgroup
+
+struct LnTile {
+    alignas(16) float x[2][kLnRows][kLnPitch];
+    float mu[kLnRows];
+    float rs[kLnRows];
+};
+
+// Loads of one tile (columns c0 .. c0+kLnCols-1 of the block's rows) into
+// registers; out-of-range elements are left as 0 and never consumed.  VEC
+// (x 16-byte aligned, x_rs and H multiples of 4): lane t loads float4 number
+// t + 64k of the tile, so 16 consecutive lanes cover one row's 256 bytes;
+// otherwise element t + 64k.
+struct LnLoad {
+    float v[kLnPerThread];
+};
+
 template <bool VEC>
-__device__ __forceinline__ f32x4 load4(const float* p) {
+__device__ __forceinline__ void ln_load(LnLoad& L, const float* x, int64_t x_rs, int64_t row0,
+                                        int64_t rows, int64_t H, int64_t c0, int tid) {
     if constexpr (VEC) {
-        return *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+        for (int k = 0; k < kLnPerThread / 4; ++k) {
+            const int q = tid + k * kLnThreads;
+            const int r = q / (kLnCols / 4), c = 4 * (q % (kLnCols / 4));
+            f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (row0 + r < rows && c0 + c < H)
+                v = *reinterpret_cast<const f32x4*>(x + (row0 + r) * x_rs + c0 + c);
+            L.v[4 * k] = v.x;
+            L.v[4 * k + 1] = v.y;
+            L.v[4 * k + 2] = v.z;
+            L.v[4 * k + 3] = v.w;
+        }
     } else {
-        f32x4 v;
-        v.x = p[0];
-        v.y = p[1];
-        v.z = p[2];
-        v.w = p[3];
-        return v;
-    }
-}
-
-template <bool VEC>
-__device__ __forceinline__ void store4(float* p, f32x4 v) {
-    if constexpr (VEC) {
-        *reinterpret_cast<f32x4*>(p) = v;
-    } else {
-        p[0] = v.x;
-        p[1] = v.y;
-        p[2] = v.z;
-        p[3] = v.w;
-    }
-}
-
-// Rows are walked in blocks of 16 floats in ascending order.  One lane owns
-// a row and there are only as many lanes as rows, so the latency of each
-// lane's loads is hidden by keeping several blocks of its row in flight: a
-// ring of blocks in registers, each refilled as soon as it has been used.
-constexpr int kRing = 8;      // blocks in flight in the two summing passes
-constexpr int kRingOut = 4;   // blocks (of x, gamma and beta) in the output pass
-
-template <bool VEC>
-__device__ __forceinline__ void load_block(const float* p, f32x4 (&b)[4]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) b[q] = load4<VEC>(p + 4 * q);
-}
-
-// f(v) for every float4 v of the first 16*nblk floats of row xr, in order.
-template <bool VEC, typename F>
-__device__ __forceinline__ void walk_row(const float* xr, int64_t nblk, F&& f) {
-    f32x4 ring[kRing][4];
-#pragma unroll
-    for (int j = 0; j < kRing; ++j)
-        if (j < nblk) load_block<VEC>(xr + 16 * j, ring[j]);
-    for (int64_t base = 0; base < nblk; base += kRing) {
-#pragma unroll
-        for (int j = 0; j < kRing; ++j) {
-            const int64_t blk = base + j;
-            if (blk < nblk) {
-                f32x4 cur[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) cur[q] = ring[j][q];
-                if (blk + kRing < nblk) load_block<VEC>(xr + 16 * (blk + kRing), ring[j]);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) f(cur[q]);
-            }
+        for (int k = 0; k < kLnPerThread; ++k) {
+            const int e = tid + k * kLnThreads;
+            const int r = e / kLnCols, c = e % kLnCols;
+            L.v[k] = (row0 + r < rows && c0 + c < H) ? x[(row0 + r) * x_rs + c0 + c] : 0.0f;
         }
     }
 }
 
-// One lane per row (the sums over a row are the fixed-order dimension; rows
-// are free).  VEC: x, y, gamma, beta 16-byte aligned and x_rs, y_rs, H
-// multiples of 4.  y may be x itself with y_rs == x_rs: a lane rewrites only
-// its own row, after its last read of each element.
-template <bool VEC>
-__global__ __launch_bounds__(64) void repops_layernorm_kernel(
-    const float* x, int64_t x_rs, const float* __restrict__ gamma,
-    const float* __restrict__ beta, float* y, int64_t y_rs, int64_t rows, int64_t H, float eps,
-    float* __restrict__ mean_out, float* __restrict__ rstd_out) {
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (r >= rows) return;
-    const float* xr = x + r * x_rs;
-    float* yr = y + r * y_rs;
-    const int64_t nblk = H >> 4;
-    const int64_t tail = nblk << 4;
-    const float fh = static_cast<float>(H);
-
-    // pass 1: S = ((+0 + x_0) + x_1) + ...
-    float s = 0.0f;
-    walk_row<VEC>(xr, nblk, [&](f32x4 v) {
-        s = s + v.x;
-        s = s + v.y;
-        s = s + v.z;
-        s = s + v.w;
-    });
-    for (int64_t i = tail; i < H; ++i) s = s + xr[i];
-    const float mu = s / fh;
-
-    // pass 2: S2 = sum of (x_i - mu)^2 in the same order
-    float s2 = 0.0f;
-    walk_row<VEC>(xr, nblk, [&](f32x4 v) {
-        const f32x4 d = v - mu;
-        const f32x4 sq = d * d;
-        s2 = s2 + sq.x;
-        s2 = s2 + sq.y;
-        s2 = s2 + sq.z;
-        s2 = s2 + sq.w;
-    });
-    for (int64_t i = tail; i < H; ++i) {
-        const float d = xr[i] - mu;
-        const float sq = d * d;
-        s2 = s2 + sq;
+// Moves a tile from registers into LDS buffer buf (the inverse of ln_load's
+// mapping).  PASS 0 stores x; PASS 1 stores (x - mu_r)^2, each element as
+// d = x - mu_r and then d * d (every lane computes the same two rounded
+// operations the definition names, so which lane does it does not matter);
+// the owner lanes then only add.
+template <int PASS, bool VEC>
+__device__ __forceinline__ void ln_store(const LnLoad& L, LnTile& T, int buf, int tid) {
+#pragma unroll
+    for (int k = 0; k < kLnPerThread; ++k) {
+        int r, c;
+        if constexpr (VEC) {
+            const int q = tid + (k / 4) * kLnThreads;
+            r = q / (kLnCols / 4);
+            c = 4 * (q % (kLnCols / 4)) + k % 4;
+        } else {
+            const int e = tid + k * kLnThreads;
+            r = e / kLnCols;
+            c = e % kLnCols;
+        }
+        float v = L.v[k];
+        if constexpr (PASS == 1) {
+            const float d = v - T.mu[r];
+            v = d * d;
+        }
+        T.x[buf][r][c] = v;
     }
-    const float var = s2 / fh;
-    const float ve = var + eps;
-    const float sd = __builtin_sqrtf(ve);
-    const float rs = 1.0f / sd;
+}
 
-    // pass 3: y_i = ((x_i - mu) * rstd) * gamma_i + beta_i, with blocks of x,
-    // gamma and beta in flight.
-    {
-        f32x4 rx[kRingOut][4], rg[kRingOut][4], rb[kRingOut][4];
-        auto fill = [&](int j, int64_t blk) {
-            load_block<VEC>(xr + 16 * blk, rx[j]);
-            if (gamma) load_block<VEC>(gamma + 16 * blk, rg[j]);
-            if (beta) load_block<VEC>(beta + 16 * blk, rb[j]);
-        };
+// PASS 0: s = s + x; PASS 1: d = x - mu, s = s + d*d; PASS 2: y.
+// One pass over the block's rows.  Tiles are loaded kLnDepth ahead into a
+// ring of registers; tile t+1 moves from the ring into the LDS buffer the
+// consumers are not reading while they consume tile t.
+// PASS 0 returns S = sum of x_i, PASS 1 S2 = sum of (x_i - mu)^2, both from
+// +0 in ascending i (in the owner lane of each row; T.mu holds the means for
+// PASS 1).
+template <int PASS, bool VEC>
+__device__ __forceinline__ float ln_pass(LnTile& T, const float* x, int64_t x_rs, int64_t row0,
+                                         int64_t rows, int64_t H, int tid) {
+    const int64_t ntiles = (H + kLnCols - 1) / kLnCols;
+    const bool owner = tid < kLnRows && row0 + tid < rows;
+    float s = 0.0f;
+    LnLoad ring[kLnDepth];
 #pragma unroll
-        for (int j = 0; j < kRingOut; ++j)
-            if (j < nblk) fill(j, j);
-        for (int64_t base = 0; base < nblk; base += kRingOut) {
+    for (int j = 0; j < kLnDepth; ++j)
+        if (j < ntiles) ln_load<VEC>(ring[j], x, x_rs, row0, rows, H, j * kLnCols, tid);
+    ln_store<PASS, VEC>(ring[0], T, 0, tid);
+    __syncthreads();
+    for (int64_t base = 0; base < ntiles; base += kLnDepth) {
 #pragma unroll
-            for (int j = 0; j < kRingOut; ++j) {
-                const int64_t blk = base + j;
-                if (blk < nblk) {
-                    f32x4 t[4];
+        for (int j = 0; j < kLnDepth; ++j) {
+            const int64_t t = base + j;
+            if (t >= ntiles) break;
+            const int buf = static_cast<int>(t & 1);
+            const int64_t c0 = t * kLnCols;
+            // ring[j] held tile t, already in LDS: refill it with tile t + depth
+            if (t + kLnDepth < ntiles)
+                ln_load<VEC>(ring[j], x, x_rs, row0, rows, H, c0 + kLnDepth * kLnCols, tid);
+            const int64_t left = H - c0;
+            const int cols = left < kLnCols ? static_cast<int>(left) : kLnCols;
+            if (owner) {
+                if (cols == kLnCols) {
+                    // A full tile: all 64 values (and gamma, beta) into
+                    // registers first, then the chain in column order.
+                    f32x4 v[kLnCols / 4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const f32x4 d = rx[j][q] - mu;
-                        t[q] = d * rs;
-                        if (gamma) t[q] = t[q] * rg[j][q];
-                        if (beta) t[q] = t[q] + rb[j][q];
+                    for (int q = 0; q < kLnCols / 4; ++q)
+                        v[q] = *reinterpret_cast<const f32x4*>(&T.x[buf][tid][4 * q]);
+#pragma unroll
+                    for (int q = 0; q < kLnCols / 4; ++q) {
+                        s = s + v[q].x;
+                        s = s + v[q].y;
+                        s = s + v[q].z;
+                        s = s + v[q].w;
                     }
-                    if (blk + kRingOut < nblk) fill(j, blk + kRingOut);
+                } else {
+                    for (int c = 0; c < cols; ++c) s = s + T.x[buf][tid][c];
+                }
+            }
+            if (t + 1 < ntiles) ln_store<PASS, VEC>(ring[(j + 1) % kLnDepth], T, buf ^ 1, tid);
+            __syncthreads();
+        }
+    }
+    return s;
+}
+
+// y = ((x - mu) * rstd) * gamma + beta for W consecutive elements (W = 4:
+// 16-byte accesses).
+template <int W>
+struct LnVec {
+    float v[W];
+};
+
+template <int W>
+__device__ __forceinline__ LnVec<W> ln_get(const float* p) {
+    LnVec<W> o;
+    if constexpr (W == 4) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+        o.v[0] = a.x;
+        o.v[1] = a.y;
+        o.v[2] = a.z;
+        o.v[3] = a.w;
+    } else {
+        o.v[0] = p[0];
+    }
+    return o;
+}
+
+template <int W>
+__device__ __forceinline__ void ln_put(float* p, const LnVec<W>& o) {
+    if constexpr (W == 4) {
+        f32x4 a;
+        a.x = o.v[0];
+        a.y = o.v[1];
+        a.z = o.v[2];
+        a.w = o.v[3];
+        *reinterpret_cast<f32x4*>(p) = a;
+    } else {
+        p[0] = o.v[0];
+    }
+}
+
+// Pass 3 has no order to keep: every lane computes outputs, consecutive lanes
+// on consecutive W-element groups of a row, four rows and four groups per
+// lane at a time so that sixteen loads are in flight.  y may be x itself with
+// y_rs == x_rs: each element is read and then written by one lane, after both
+// summing passes, and other workgroups own other rows.
+template <int W>
+__device__ __forceinline__ void ln_output(const LnTile& T, const float* x, int64_t x_rs,
+                                          const float* gamma, const float* beta, float* y,
+                                          int64_t y_rs, int64_t row0, int nr, int64_t H,
+                                          int tid) {
+    constexpr int RU = 4, CU = 4;
+    const int64_t groups = H / W;
+    for (int r0 = 0; r0 < nr; r0 += RU) {
+        for (int64_t gb = 0; gb < groups; gb += CU * kLnThreads) {
+            LnVec<W> v[RU][CU], g[CU], b[CU];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) store4<VEC>(yr + 16 * blk + 4 * q, t[q]);
+            for (int u = 0; u < CU; ++u) {
+                const int64_t gi = gb + tid + u * kLnThreads;
+                if (gi < groups) {
+                    if (gamma) g[u] = ln_get<W>(gamma + gi * W);
+                    if (beta) b[u] = ln_get<W>(beta + gi * W);
+#pragma unroll
+                    for (int rr = 0; rr < RU; ++rr)
+                        if (r0 + rr < nr) v[rr][u] = ln_get<W>(x + (row0 + r0 + rr) * x_rs + gi * W);
+                }
+            }
+#pragma unroll
+            for (int rr = 0; rr < RU; ++rr) {
+                if (r0 + rr >= nr) break;
+                const float m = T.mu[r0 + rr], q = T.rs[r0 + rr];
+#pragma unroll
+                for (int u = 0; u < CU; ++u) {
+                    const int64_t gi = gb + tid + u * kLnThreads;
+                    if (gi < groups) {
+                        LnVec<W> o;
+#pragma unroll
+                        for (int w = 0; w < W; ++w) {
+                            const float d = v[rr][u].v[w] - m;
+                            float t = d * q;
+                            if (gamma) t = t * g[u].v[w];
+                            if (beta) t = t + b[u].v[w];
+                            o.v[w] = t;
+                        }
+                        ln_put<W>(y + (row0 + r0 + rr) * y_rs + gi * W, o);
+                    }
                 }
             }
         }
     }
-    for (int64_t i = tail; i < H; ++i) {
-        const float d = xr[i] - mu;
-        float t = d * rs;
-        if (gamma) t = t * gamma[i];
-        if (beta) t = t + beta[i];
-        yr[i] = t;
+}
+
+// VEC: x, y, gamma, beta 16-byte aligned; x_rs, y_rs and H multiples of 4.
+template <bool VEC>
+__global__ __launch_bounds__(kLnThreads) void repops_layernorm_kernel(
+    const float* x, int64_t x_rs, const float* __restrict__ gamma,
+    const float* __restrict__ beta, float* y, int64_t y_rs, int64_t rows, int64_t H, float eps,
+    float* __restrict__ mean_out, float* __restrict__ rstd_out) {
+    __shared__ LnTile T;
+    const int tid = static_cast<int>(threadIdx.x);
+    const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kLnRows;
+    const float fh = static_cast<float>(H);
+
+    // pass 1: S = ((+0 + x_0) + x_1) + ...;  mu = S / H (owner lanes)
+    const float s = ln_pass<0, VEC>(T, x, x_rs, row0, rows, H, tid);
+    const float mu = s / fh;
+    if (tid < kLnRows) T.mu[tid] = mu;
+    __syncthreads();
+
+    // pass 2: S2 = sum of (x_i - mu)^2 in the same order; rstd = 1/sqrt(S2/H + eps)
+    const float s2 = ln_pass<1, VEC>(T, x, x_rs, row0, rows, H, tid);
+    const float var = s2 / fh;
+    const float ve = var + eps;
+    const float sd = __builtin_sqrtf(ve);
+    const float rs = 1.0f / sd;
+    if (tid < kLnRows) {
+        T.rs[tid] = rs;
+        if (row0 + tid < rows) {
+            if (mean_out) mean_out[row0 + tid] = mu;
+            if (rstd_out) rstd_out[row0 + tid] = rs;
+        }
     }
-    if (mean_out) mean_out[r] = mu;
-    if (rstd_out) rstd_out[r] = rs;
+    __syncthreads();
+
+    // pass 3: y_i = ((x_i - mu) * rstd) * gamma_i + beta_i, all lanes
+    const int nr = rows - row0 < kLnRows ? static_cast<int>(rows - row0) : kLnRows;
+    ln_output<VEC ? 4 : 1>(T, x, x_rs, gamma, beta, y, y_rs, row0, nr, H, tid);
 }
 
 }  // namespace
@@ -277,13 +388,13 @@ int launch_unary(int op, const float* x, float* y, int64_t n, bool vec, void* st
 int launch_layernorm(const float* x, int64_t x_rs, const float* gamma, const float* beta, float* y,
                      int64_t y_rs, int64_t rows, int64_t H, float eps, float* mean, float* rstd,
                      bool vec, void* stream) {
-    const int64_t blocks = (rows + 63) / 64;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t blocks = (rows + kLnRows - 1) / kLnRows;
     using Fn = void (*)(const float*, int64_t, const float*, const float*, float*, int64_t,
                         int64_t, int64_t, float, float*, float*);
     Fn fn = vec ? repops_layernorm_kernel<true> : repops_layernorm_kernel<false>;
-    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(64), 0, s, x, x_rs, gamma,
-                       beta, y, y_rs, rows, H, eps, mean, rstd);
+    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(kLnThreads), 0,
+                       static_cast<hipStream_t>(stream), x, x_rs, gamma, beta, y, y_rs, rows, H,
+                       eps, mean, rstd);
     return static_cast<int>(hipGetLastError());
 }
 
