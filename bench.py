@@ -70,6 +70,36 @@ def committed_traffic(variant_name):
         return None
 
 
+def calibration_copy(torch, dev):
+    """Three 1 GiB device-to-device copies: a kernel of known traffic that the
+    counter passes read to scale FETCH_SIZE and WRITE_SIZE."""
+    n = 256 * 1024 * 1024  # floats: 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copy calibration: 3 copies of %d bytes" % (4 * n))
+    del src, dst
+
+
+def traffic_from(profile, kernel_src):
+    """traffic_bytes_per_launch from a committed counter summary under
+    profiles/, or None when it is missing or was taken on another version of
+    the kernel source."""
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    fields = dict(re.findall(r"^([a-z_0-9]+):\s*(\S+)\s*$", open(path).read(), re.M))
+    src = os.path.join(ROOT, "bit_reproducible_fp32_amd", "csrc", kernel_src)
+    if fields.get("kernel_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def timed_region(torch, stream, step, steps):
     """Run `steps` steps back to back between one pair of HIP events on the
     launch stream.  Returns (host wall seconds, event milliseconds per step):
@@ -242,14 +272,7 @@ def main():
         del ref
 
     if args.calibrate_copy:
-        n = 256 * 1024 * 1024  # floats: 1 GiB
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log("copy calibration: 3 copies of %d bytes" % (4 * n))
-        del src, dst
+        calibration_copy(torch, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -344,8 +367,6 @@ def bench_batched(args, torch, rp, inputs, dev):
 
 
 HBM_PEAK_GBS = 8000.0
-FOLD_KERNEL_SRC = os.path.join(ROOT, "bit_reproducible_fp32_amd", "csrc", "repops_fold.hip")
-FOLD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fold_k8_d64M_traffic.txt")
 
 
 def bench_fold(args, torch, rp, inputs, dev):
@@ -394,12 +415,10 @@ def bench_fold(args, torch, rp, inputs, dev):
         cpu = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": "the whole workload (k=%d, d=%d) in %.1f s, single thread" % (w.k, w.d, dt)}
 
-    traffic = None
-    if os.path.exists(FOLD_TRAFFIC_FILE):
-        fields = dict(re.findall(r"^([a-z_0-9]+):\s*(\S+)\s*$", open(FOLD_TRAFFIC_FILE).read(), re.M))
-        if fields.get("kernel_source_sha256") == hashlib.sha256(
-                open(FOLD_KERNEL_SRC, "rb").read()).hexdigest():
-            traffic = float(fields.get("traffic_bytes_per_launch", "nan"))
+    traffic = traffic_from("fold_k8_d64M_traffic.txt", "repops_fold.hip") \
+        if w.name == "fold_k8_d64M" else None
+    if args.calibrate_copy:
+        calibration_copy(torch, dev)
     rec = {
         "metric": "fixed-order gradient average + SGD step, algorithmic GB/s, bit-exact",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -510,6 +529,9 @@ def bench_merkle(args, torch, rp, inputs, dev):
               file=sys.stderr)
         sys.exit(3)
     log("root %s matches the oracle; referee verdict %s" % (gpu_root.hex(), verdict))
+    if args.calibrate_copy:
+        calibration_copy(torch, dev)
+    traffic = traffic_from("%s_traffic.txt" % w.name, "repops_merkle.hip")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
@@ -526,7 +548,7 @@ def bench_merkle(args, torch, rp, inputs, dev):
                    "nbytes": nbytes, "leaf_bytes": w.leaf_bytes, "compressions": comp},
         "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": VALU_PEAK_TSLOTS,
                      "unit": "T VALU issue slots/s", "frac": round(achieved / VALU_PEAK_TSLOTS, 4),
-                     "traffic": None},
+                     "traffic": traffic},
         "cpu_baseline": cpu, "bitexact": True,
         "kernel_ms": {"mean": round(k_avg, 5)},
         "referee": {"matmul_ms": round(float(np.median(mm_ms)), 4),
@@ -587,6 +609,9 @@ def bench_ops(args, torch, rp, inputs, dev):
               file=sys.stderr)
         sys.exit(3)
     log("bit-exact on all %d outputs" % n)
+    if args.calibrate_copy:
+        calibration_copy(torch, dev)
+    traffic = traffic_from("%s_traffic.txt" % w.name, "repops_ops.hip")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
@@ -600,7 +625,8 @@ def bench_ops(args, torch, rp, inputs, dev):
         "config": {"workload": "%s rows=%d H=%d" % (w.name, w.rows, w.H), "rows": w.rows,
                    "H": w.H},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
         "cpu_baseline": cpu, "bitexact": True,
         "kernel_ms": {"mean": round(k_avg, 5)},
     }
