@@ -247,21 +247,27 @@ def test_kernel_descriptors_ieee_denormals_and_rne():
         assert re.search(r"\.amdhsa_float_round_mode_32 0\b", d), name
 
 
-def test_tiled_kernels_do_not_spill():
+def test_no_kernel_spills_or_uses_scratch():
+    """Every kernel keeps its state in registers and LDS: no spills and no
+    per-lane scratch memory."""
     text = open(ASM).read()
+    seen = 0
     for block in text.split("  - .agpr_count:")[1:]:
         name = re.search(r"\.name:\s+(\S+)", block).group(1)
-        if "tiled_kernel" not in name:
+        if "repops" not in name:
             continue
+        seen += 1
         spill = int(re.search(r"\.vgpr_spill_count:\s+(\d+)", block).group(1))
         priv = int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", block).group(1))
         assert spill == 0 and priv == 0, name
+    assert seen >= 30
 
 
 def test_assembly_matches_the_library_build():
-    """The scanned assembly is at least as new as the kernel source."""
-    src = os.path.join(ROOT, "bit_reproducible_fp32_amd", "csrc", "repops_kernels.hip")
-    assert os.path.getmtime(ASM) >= os.path.getmtime(src) - 1
+    """The scanned assembly is at least as new as every kernel source."""
+    from bit_reproducible_fp32_amd import build
+    for src in build.KERNEL_SOURCES:
+        assert os.path.getmtime(ASM) >= os.path.getmtime(src) - 1, src
 
 
 def bok(**kw):
