@@ -370,6 +370,137 @@ __global__ __launch_bounds__(kLnThreads) void repops_layernorm_kernel(
     ln_output<VEC ? 4 : 1>(T, x, x_rs, gamma, beta, y, y_rs, row0, nr, H, tid);
 }
 
+// The resident form, for rows short enough that kLnResRows of them fit in
+// LDS: the block is read from memory once; lane r sums row r from LDS; then
+// every lane replaces x_i by d_i = x_i - mu (the operation the definition
+// names, rounded once), lane r sums d_i * d_i, and every lane writes
+// y_i = (d_i * rstd) * gamma_i + beta_i.  A small block lets many workgroups
+// share a CU, so one block's loads overlap another's sums.  ld_h: the row
+// pitch in LDS (H rounded up to 4, plus 4).
+constexpr int kLnResRows = 4;
+
+template <bool VEC>
+__global__ __launch_bounds__(kLnThreads) void repops_layernorm_resident_kernel(
+    const float* x, int64_t x_rs, const float* __restrict__ gamma,
+    const float* __restrict__ beta, float* y, int64_t y_rs, int64_t rows, int64_t H, int ld_h,
+    float eps, float* __restrict__ mean_out, float* __restrict__ rstd_out) {
+    extern __shared__ float4 ln_dyn[];
+    float* blk = reinterpret_cast<float*>(ln_dyn);
+    __shared__ float mu_s[kLnResRows], rs_s[kLnResRows];
+    const int tid = static_cast<int>(threadIdx.x);
+    const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kLnResRows;
+    const int nr = rows - row0 < kLnResRows ? static_cast<int>(rows - row0) : kLnResRows;
+    constexpr int W = VEC ? 4 : 1;
+    const int groups = static_cast<int>(H / W);  // W-element groups per row
+    const int total = nr * groups;
+    const float fh = static_cast<float>(H);
+
+    // the block into LDS, sixteen loads in flight per lane
+    for (int base = 0; base < total; base += 16 * kLnThreads) {
+        LnVec<W> v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int e = base + u * kLnThreads + tid;
+            if (e < total) {
+                const int r = e / groups, gi = e - r * groups;
+                v[u] = ln_get<W>(x + (row0 + r) * x_rs + static_cast<int64_t>(gi) * W);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int e = base + u * kLnThreads + tid;
+            if (e < total) {
+                const int r = e / groups, gi = e - r * groups;
+                ln_put<W>(blk + r * ld_h + gi * W, v[u]);
+            }
+        }
+    }
+    __syncthreads();
+
+    // S = ((+0 + x_0) + x_1) + ...;  mu = S / H
+    const int64_t H64 = H & ~int64_t(63);
+    if (tid < nr) {
+        const float* row = blk + tid * ld_h;
+        float s = 0.0f;
+        for (int64_t c = 0; c < H64; c += 64) {
+            f32x4 v[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) v[q] = *reinterpret_cast<const f32x4*>(row + c + 4 * q);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                s = s + v[q].x;
+                s = s + v[q].y;
+                s = s + v[q].z;
+                s = s + v[q].w;
+            }
+        }
+        for (int64_t c = H64; c < H; ++c) s = s + row[c];
+        mu_s[tid] = s / fh;
+    }
+    __syncthreads();
+
+    // d_i = x_i - mu, in place, every lane
+    for (int e = tid; e < total; e += kLnThreads) {
+        const int r = e / groups, gi = e - r * groups;
+        float* p = blk + r * ld_h + gi * W;
+        LnVec<W> v = ln_get<W>(p);
+        const float m = mu_s[r];
+#pragma unroll
+        for (int w = 0; w < W; ++w) v.v[w] = v.v[w] - m;
+        ln_put<W>(p, v);
+    }
+    __syncthreads();
+
+    // S2 = sum of d_i * d_i in the same order; rstd = 1 / sqrt(S2 / H + eps)
+    if (tid < nr) {
+        const float* row = blk + tid * ld_h;
+        float s2 = 0.0f;
+        for (int64_t c = 0; c < H64; c += 64) {
+            f32x4 v[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) v[q] = *reinterpret_cast<const f32x4*>(row + c + 4 * q);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const f32x4 sq = v[q] * v[q];
+                s2 = s2 + sq.x;
+                s2 = s2 + sq.y;
+                s2 = s2 + sq.z;
+                s2 = s2 + sq.w;
+            }
+        }
+        for (int64_t c = H64; c < H; ++c) {
+            const float sq = row[c] * row[c];
+            s2 = s2 + sq;
+        }
+        const float var = s2 / fh;
+        const float ve = var + eps;
+        const float sd = __builtin_sqrtf(ve);
+        const float rs = 1.0f / sd;
+        rs_s[tid] = rs;
+        if (mean_out) mean_out[row0 + tid] = mu_s[tid];
+        if (rstd_out) rstd_out[row0 + tid] = rs;
+    }
+    __syncthreads();
+
+    // y_i = (d_i * rstd) * gamma_i + beta_i, every lane
+    for (int e = tid; e < total; e += kLnThreads) {
+        const int r = e / groups, gi = e - r * groups;
+        const LnVec<W> v = ln_get<W>(blk + r * ld_h + gi * W);
+        LnVec<W> g, b, o;
+        if (gamma) g = ln_get<W>(gamma + static_cast<int64_t>(gi) * W);
+        if (beta) b = ln_get<W>(beta + static_cast<int64_t>(gi) * W);
+        const float q = rs_s[r];
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            float t = v.v[w] * q;
+            if (gamma) t = t * g.v[w];
+            if (beta) t = t + b.v[w];
+            o.v[w] = t;
+        }
+        ln_put<W>(y + (row0 + r) * y_rs + static_cast<int64_t>(gi) * W, o);
+    }
+}
+
 }  // namespace
 
 int launch_unary(int op, const float* x, float* y, int64_t n, bool vec, void* stream) {
@@ -388,13 +519,27 @@ int launch_unary(int op, const float* x, float* y, int64_t n, bool vec, void* st
 int launch_layernorm(const float* x, int64_t x_rs, const float* gamma, const float* beta, float* y,
                      int64_t y_rs, int64_t rows, int64_t H, float eps, float* mean, float* rstd,
                      bool vec, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // Resident form when a block of kLnResRows rows fits in 32 KB of LDS.
+    const int64_t ld_h = ((H + 3) & ~int64_t(3)) + 4;
+    const int64_t lds = kLnResRows * ld_h * 4;
+    if (lds <= 32768) {
+        using Rn = void (*)(const float*, int64_t, const float*, const float*, float*, int64_t,
+                            int64_t, int64_t, int, float, float*, float*);
+        Rn rn = vec ? repops_layernorm_resident_kernel<true>
+                    : repops_layernorm_resident_kernel<false>;
+        const int64_t rblocks = (rows + kLnResRows - 1) / kLnResRows;
+        hipLaunchKernelGGL(rn, dim3(static_cast<unsigned>(rblocks)), dim3(kLnThreads),
+                           static_cast<unsigned>(lds), s, x, x_rs, gamma, beta, y, y_rs, rows, H,
+                           static_cast<int>(ld_h), eps, mean, rstd);
+        return static_cast<int>(hipGetLastError());
+    }
     const int64_t blocks = (rows + kLnRows - 1) / kLnRows;
     using Fn = void (*)(const float*, int64_t, const float*, const float*, float*, int64_t,
                         int64_t, int64_t, float, float*, float*);
     Fn fn = vec ? repops_layernorm_kernel<true> : repops_layernorm_kernel<false>;
-    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(kLnThreads), 0,
-                       static_cast<hipStream_t>(stream), x, x_rs, gamma, beta, y, y_rs, rows, H,
-                       eps, mean, rstd);
+    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(kLnThreads), 0, s, x, x_rs,
+                       gamma, beta, y, y_rs, rows, H, eps, mean, rstd);
     return static_cast<int>(hipGetLastError());
 }
 
