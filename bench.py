@@ -175,8 +175,8 @@ def main():
         args.warmup = 200 if short else 5
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the fixed-order matmul shards over output "
-              "tiles with no exchange, and this build runs and reports a single GPU. "
+        print("bench.py measures one GPU only (the fixed-order matmul shards over output "
+              "tiles with no exchange, so per-GPU throughput is the single-GPU figure). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
