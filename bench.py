@@ -337,6 +337,10 @@ def bench_batched(args, torch, rp, inputs, dev):
                   file=sys.stderr)
             sys.exit(3)
     log("bit-exact on sampled outputs of every fifth head")
+    if args.calibrate_copy:
+        calibration_copy(torch, dev)
+    traffic = traffic_from("%s_traffic.txt" % w.name, "repops_kernels.hip") \
+        if args.variant is None else None
     flops = float(w.flops)
     ms_per_step = wall * 1e3 / args.steps
     achieved = flops / (k_avg * 1e-3) / 1e12
@@ -359,7 +363,7 @@ def bench_batched(args, torch, rp, inputs, dev):
         "config": {"workload": "%s batch=%d M=%d N=%d K=%d" % (w.name, w.batch, w.M, w.N, w.K)},
         "roofline": {"bound": "alu", "achieved": round(achieved, 4), "peak": UNFUSED_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / UNFUSED_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": traffic},
         "cpu_baseline": cpu, "bitexact_sampled": True,
         "kernel_ms": {"mean": round(k_avg, 4)},
     }
