@@ -501,6 +501,187 @@ __global__ __launch_bounds__(kLnThreads) void repops_layernorm_resident_kernel(
     }
 }
 
+// Lane 4q + g of the result holds lane 4q + (g + 3) % 4 of s: one step of a
+// ring around each quad (DPP quad permutation [3, 0, 1, 2]).
+__device__ __forceinline__ float quad_ring_step(float s) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x93, 0xF, 0xF, false));
+}
+
+// Every lane of a quad receives lane 3's s (quad permutation [3, 3, 3, 3]).
+__device__ __forceinline__ float quad_from_last(float s) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0xFF, 0xF, 0xF, false));
+}
+
+// The register-resident form, for rows of at most 4 * S elements.  A row
+// belongs to one quad of lanes (16 rows per wave) and is dealt out in pieces
+// of 8 elements: piece j of lane g is elements [32 j + 8 g, 32 j + 8 g + 8),
+// so that the quad reads and writes 128 contiguous bytes per piece.  Every
+// row is on chip at once and x is read once.
+//
+// A fixed-order sum walks the pieces in row order, which visits the lanes of
+// the quad in turn: before each piece the running sums take one step around
+// the quad, so lane g receives the sum that lane g - 1 has just carried
+// through its piece, and adds its own 8 elements in ascending order.  All
+// four lanes run every step (three of them on values that the next steps
+// overwrite), so the adds that reach the result are exactly x_0, x_1, ...
+// in ascending order from +0.  The padding past H holds +0, which leaves a
+// running sum unchanged: it starts at +0 and so is never -0, and s + (+0) == s
+// for every other s (a NaN stays a NaN).
+//
+// FULL (16 live rows of exactly 4 * S elements) drops every bounds test, so
+// that the loads are unconditional and issued in piece order, and the sum
+// can start on the first piece while the later ones are still in flight.
+template <int S, bool VEC, bool FULL>
+__device__ __forceinline__ void ln_regs_group(const float* xs, float* ys, int hl, bool live,
+                                              int64_t row, int seg, float fh, float eps,
+                                              const float* gs, const float* bs,
+                                              float* __restrict__ mean_out,
+                                              float* __restrict__ rstd_out) {
+    constexpr int kPieces = S / 8;
+    float v[S];
+    if constexpr (VEC) {
+#pragma unroll
+        for (int q = 0; q < S / 4; ++q) {
+            const int o = 32 * (q >> 1) + 4 * (q & 1);
+            f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (FULL || o < hl) a = *reinterpret_cast<const f32x4*>(xs + o);
+            v[4 * q] = a.x;
+            v[4 * q + 1] = a.y;
+            v[4 * q + 2] = a.z;
+            v[4 * q + 3] = a.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+            const int o = 32 * (i >> 3) + (i & 7);
+            v[i] = (FULL || o < hl) ? xs[o] : 0.0f;
+        }
+    }
+
+    // S = ((+0 + x_0) + x_1) + ...
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            s = quad_ring_step(s);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) s = s + v[8 * j + k];
+        }
+    }
+    s = quad_from_last(s);
+    const float mu = s / fh;
+
+    // d_i = x_i - mu in place (+0 in the padding); S2 = sum of d_i * d_i
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+        const int o = 32 * (i >> 3) + (i & 7);
+        v[i] = (FULL || o < hl) ? v[i] - mu : 0.0f;
+    }
+    float s2 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) {
+        float sq[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sq[k] = v[8 * j + k] * v[8 * j + k];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            s2 = quad_ring_step(s2);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) s2 = s2 + sq[k];
+        }
+    }
+    s2 = quad_from_last(s2);
+    const float var = s2 / fh;
+    const float ve = var + eps;
+    const float sd = __builtin_sqrtf(ve);
+    const float rs = 1.0f / sd;
+    if (live && seg == 0) {
+        if (mean_out) mean_out[row] = mu;
+        if (rstd_out) rstd_out[row] = rs;
+    }
+
+    // y_i = (d_i * rstd) * gamma_i + beta_i
+    if constexpr (VEC) {
+#pragma unroll
+        for (int q = 0; q < S / 4; ++q) {
+            const int o = 32 * (q >> 1) + 4 * (q & 1);
+            if (FULL || o < hl) {
+                f32x4 t;
+                t.x = v[4 * q] * rs;
+                t.y = v[4 * q + 1] * rs;
+                t.z = v[4 * q + 2] * rs;
+                t.w = v[4 * q + 3] * rs;
+                t = t * *reinterpret_cast<const f32x4*>(gs + o);
+                t = t + *reinterpret_cast<const f32x4*>(bs + o);
+                *reinterpret_cast<f32x4*>(ys + o) = t;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+            const int o = 32 * (i >> 3) + (i & 7);
+            if (FULL || o < hl) {
+                float t = v[i] * rs;
+                t = t * gs[o];
+                t = t + bs[o];
+                ys[o] = t;
+            }
+        }
+    }
+}
+
+template <int S, bool VEC>
+__global__ __launch_bounds__(64) void repops_layernorm_regs_kernel(
+    const float* x, int64_t x_rs, const float* __restrict__ gamma,
+    const float* __restrict__ beta, float* y, int64_t y_rs, int64_t rows, int64_t H, float eps,
+    float* __restrict__ mean_out, float* __restrict__ rstd_out) {
+    // gamma and beta, staged once per workgroup.  A missing gamma is staged
+    // as 1 and a missing beta as -0: t * 1 == t and t + (-0) == t for every
+    // binary32 t (signed zeros, infinities and NaN included), so the output
+    // step needs no branch and matches skipping the operation.
+    __shared__ __align__(16) float ln_g[4 * S];
+    __shared__ __align__(16) float ln_b[4 * S];
+    const int lane = static_cast<int>(threadIdx.x);
+    const int seg = lane & 3;
+    const int64_t groups = (rows + 15) / 16;
+    const float fh = static_cast<float>(H);
+    const int hi = static_cast<int>(H);
+    if constexpr (VEC) {
+        for (int c = 4 * lane; c < 4 * S; c += 256) {
+            f32x4 gv = {1.0f, 1.0f, 1.0f, 1.0f}, bv = {-0.0f, -0.0f, -0.0f, -0.0f};
+            if (gamma && c < hi) gv = *reinterpret_cast<const f32x4*>(gamma + c);
+            if (beta && c < hi) bv = *reinterpret_cast<const f32x4*>(beta + c);
+            *reinterpret_cast<f32x4*>(ln_g + c) = gv;
+            *reinterpret_cast<f32x4*>(ln_b + c) = bv;
+        }
+    } else {
+        for (int c = lane; c < 4 * S; c += 64) {
+            ln_g[c] = gamma && c < hi ? gamma[c] : 1.0f;
+            ln_b[c] = beta && c < hi ? beta[c] : -0.0f;
+        }
+    }
+    __syncthreads();
+    for (int64_t rg = blockIdx.x; rg < groups; rg += gridDim.x) {
+        const int64_t row = rg * 16 + (lane >> 2);
+        const bool live = row < rows;
+        // element 32 j + 8 seg + k of the row is at offset o = 32 j + k from
+        // xs, and exists when o < hl
+        const int hl = live ? hi - 8 * seg : 0;
+        const float* xs = x + (live ? row : 0) * x_rs + 8 * seg;
+        float* ys = y + (live ? row : 0) * y_rs + 8 * seg;
+        const bool full = (rg + 1) * 16 <= rows && hi == 4 * S;
+        if (full)
+            ln_regs_group<S, VEC, true>(xs, ys, hl, live, row, seg, fh, eps, ln_g + 8 * seg,
+                                        ln_b + 8 * seg, mean_out, rstd_out);
+        else
+            ln_regs_group<S, VEC, false>(xs, ys, hl, live, row, seg, fh, eps, ln_g + 8 * seg,
+                                         ln_b + 8 * seg, mean_out, rstd_out);
+    }
+}
+
 }  // namespace
 
 int launch_unary(int op, const float* x, float* y, int64_t n, bool vec, void* stream) {
@@ -520,6 +701,24 @@ int launch_layernorm(const float* x, int64_t x_rs, const float* gamma, const flo
                      int64_t y_rs, int64_t rows, int64_t H, float eps, float* mean, float* rstd,
                      bool vec, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // Register-resident form for rows of at most 768 elements (the row and
+    // its squared deviations are both held: 2 * 192 registers per lane).
+    if (H <= 768) {
+        using Gn = void (*)(const float*, int64_t, const float*, const float*, float*, int64_t,
+                            int64_t, int64_t, float, float*, float*);
+        Gn gn;
+        if (H <= 256)
+            gn = vec ? repops_layernorm_regs_kernel<64, true> : repops_layernorm_regs_kernel<64, false>;
+        else if (H <= 512)
+            gn = vec ? repops_layernorm_regs_kernel<128, true> : repops_layernorm_regs_kernel<128, false>;
+        else
+            gn = vec ? repops_layernorm_regs_kernel<192, true> : repops_layernorm_regs_kernel<192, false>;
+        const int64_t groups = (rows + 15) / 16;
+        const int64_t gblocks = groups < (int64_t(1) << 20) ? groups : (int64_t(1) << 20);
+        hipLaunchKernelGGL(gn, dim3(static_cast<unsigned>(gblocks)), dim3(64), 0, s, x, x_rs,
+                           gamma, beta, y, y_rs, rows, H, eps, mean, rstd);
+        return static_cast<int>(hipGetLastError());
+    }
     // Resident form when a block of kLnResRows rows fits in 32 KB of LDS.
     const int64_t ld_h = ((H + 3) & ~int64_t(3)) + 4;
     const int64_t lds = kLnResRows * ld_h * 4;

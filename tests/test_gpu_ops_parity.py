@@ -156,8 +156,10 @@ def check_layernorm(x, gamma, beta, eps, **kw):
         same_bits(g, w, what)
 
 
-@pytest.mark.parametrize("rows,H", [(1, 1), (3, 2), (5, 3), (64, 4), (65, 5), (63, 768),
-                                    (130, 1023), (7, 4096), (4099, 8)])
+@pytest.mark.parametrize("rows,H", [(1, 1), (3, 2), (5, 3), (64, 4), (65, 5), (17, 63),
+                                    (31, 256), (16, 257), (33, 512), (47, 513), (63, 768),
+                                    (18, 767), (19, 769), (130, 1023), (7, 2044), (9, 2045),
+                                    (7, 4096), (4099, 8)])
 def test_layernorm_shapes(rows, H):
     say("layernorm rows=%d H=%d" % (rows, H))
     rng = np.random.default_rng(rows * 31 + H)
