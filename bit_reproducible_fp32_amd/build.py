@@ -14,6 +14,7 @@ Flags that matter for the arithmetic:
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -48,27 +49,53 @@ def _manifest_defines():
     return ["-DREPOPS_BUILD_FLAGS=\"%s\"" % flags, "-DREPOPS_OFFLOAD_ARCH=\"%s\"" % ARCH]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into librepops.so and write the gfx950 assembly."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *COMMON, *FP_FLAGS, *DEVICE_FLAGS, *_manifest_defines(), "-shared",
-           "-o", tmp, *SOURCES]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    # Device-only assembly of every kernel source, for the instruction scan.
-    parts = []
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into librepops.so and write the gfx950 assembly.
+
+    The sources compile to objects in parallel, next to the device-only
+    assembly of each kernel source (for the instruction scan); the objects
+    then link into the library."""
+    tag = "%d" % os.getpid()
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    jobs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, os.path.basename(src) + "." + tag + ".o")
+        objs.append(obj)
+        jobs.append([HIPCC, *COMMON, *FP_FLAGS, *DEVICE_FLAGS, *_manifest_defines(), "-c",
+                     "-o", obj, src])
+    asms = []
     for src in KERNEL_SOURCES:
-        asm_tmp = ASM + ".tmp%d" % os.getpid()
-        cmd = [HIPCC, *COMMON, *FP_FLAGS, *DEVICE_FLAGS, "--cuda-device-only", "-S",
-               "-o", asm_tmp, src]
-        subprocess.run(cmd, check=True)
-        parts.append(open(asm_tmp).read())
-        os.remove(asm_tmp)
-    with open(ASM + ".tmp", "w") as f:
-        f.write("\n".join(parts))
-    os.replace(ASM + ".tmp", ASM)
+        asm = os.path.join(objdir, os.path.basename(src) + "." + tag + ".s")
+        asms.append(asm)
+        jobs.append([HIPCC, *COMMON, *FP_FLAGS, *DEVICE_FLAGS, "--cuda-device-only", "-S",
+                     "-o", asm, src])
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+    try:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as pool:
+            for f in [pool.submit(_run, cmd, verbose) for cmd in jobs]:
+                f.result()
+        tmp = LIB + ".tmp" + tag
+        _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-o", tmp, *objs], verbose)
+        os.replace(tmp, LIB)
+        with open(ASM + ".tmp", "w") as f:
+            f.write("\n".join(open(a).read() for a in asms))
+        os.replace(ASM + ".tmp", ASM)
+    finally:
+        for path in objs + asms:
+            if os.path.exists(path):
+                os.remove(path)
+        try:
+            os.rmdir(objdir)
+        except OSError:
+            pass
     return LIB
 
 

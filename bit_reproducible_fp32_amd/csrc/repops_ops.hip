@@ -125,7 +125,8 @@ __global__ __launch_bounds__(256) void repops_unary_kernel(const float* x, float
     for (int64_t e = from + t0; e < n; e += stride) y[e] = unary<OP>(x[e]);
 }
 
-// LayerNorm.  The two sums over a row are the fixed-order dimension, so one
+// LayerNorm, streaming form (rows longer than the register-resident forms
+// below hold).  The two sums over a row are the fixed-order dimension, so one
 // lane owns a row and walks it in ascending order; rows are the free
 // dimension.  To keep the loads coalesced, a workgroup of kLnThreads lanes owns
 // kLnRows consecutive rows and streams them through LDS in tiles of kLnRows x
@@ -390,181 +391,61 @@ __global__ __launch_bounds__(kLnThreads) void repops_layernorm_kernel(
     ln_output<VEC ? 4 : 1>(T, x, x_rs, gamma, beta, y, y_rs, row0, nr, H, tid);
 }
 
-// The resident form, for rows short enough that kLnResRows of them fit in
-// LDS: the block is read from memory once; lane r sums row r from LDS; then
-// every lane replaces x_i by d_i = x_i - mu (the operation the definition
-// names, rounded once), lane r sums d_i * d_i, and every lane writes
-// y_i = (d_i * rstd) * gamma_i + beta_i.  A small block lets many workgroups
-// share a CU, so one block's loads overlap another's sums.  ld_h: the row
-// pitch in LDS (H rounded up to 4, plus 4).
-constexpr int kLnResRows = 4;
-
-template <bool VEC>
-__global__ __launch_bounds__(kLnThreads) void repops_layernorm_resident_kernel(
-    const float* x, int64_t x_rs, const float* __restrict__ gamma,
-    const float* __restrict__ beta, float* y, int64_t y_rs, int64_t rows, int64_t H, int ld_h,
-    float eps, float* __restrict__ mean_out, float* __restrict__ rstd_out) {
-    extern __shared__ float4 ln_dyn[];
-    float* blk = reinterpret_cast<float*>(ln_dyn);
-    __shared__ float mu_s[kLnResRows], rs_s[kLnResRows];
-    const int tid = static_cast<int>(threadIdx.x);
-    const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kLnResRows;
-    const int nr = rows - row0 < kLnResRows ? static_cast<int>(rows - row0) : kLnResRows;
-    constexpr int W = VEC ? 4 : 1;
-    const int groups = static_cast<int>(H / W);  // W-element groups per row
-    const int total = nr * groups;
-    const float fh = static_cast<float>(H);
-
-    // the block into LDS, sixteen loads in flight per lane
-    for (int base = 0; base < total; base += 16 * kLnThreads) {
-        LnVec<W> v[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int e = base + u * kLnThreads + tid;
-            if (e < total) {
-                const int r = e / groups, gi = e - r * groups;
-                v[u] = ln_get<W>(x + (row0 + r) * x_rs + static_cast<int64_t>(gi) * W);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int e = base + u * kLnThreads + tid;
-            if (e < total) {
-                const int r = e / groups, gi = e - r * groups;
-                ln_put<W>(blk + r * ld_h + gi * W, v[u]);
-            }
-        }
-    }
-    __syncthreads();
-
-    // S = ((+0 + x_0) + x_1) + ...;  mu = S / H
-    const int64_t H64 = H & ~int64_t(63);
-    if (tid < nr) {
-        const float* row = blk + tid * ld_h;
-        float s = 0.0f;
-        for (int64_t c = 0; c < H64; c += 64) {
-            f32x4 v[16];
-#pragma unroll
-            for (int q = 0; q < 16; ++q) v[q] = *reinterpret_cast<const f32x4*>(row + c + 4 * q);
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                s = s + v[q].x;
-                s = s + v[q].y;
-                s = s + v[q].z;
-                s = s + v[q].w;
-            }
-        }
-        for (int64_t c = H64; c < H; ++c) s = s + row[c];
-        mu_s[tid] = s / fh;
-    }
-    __syncthreads();
-
-    // d_i = x_i - mu, in place, every lane
-    for (int e = tid; e < total; e += kLnThreads) {
-        const int r = e / groups, gi = e - r * groups;
-        float* p = blk + r * ld_h + gi * W;
-        LnVec<W> v = ln_get<W>(p);
-        const float m = mu_s[r];
-#pragma unroll
-        for (int w = 0; w < W; ++w) v.v[w] = v.v[w] - m;
-        ln_put<W>(p, v);
-    }
-    __syncthreads();
-
-    // S2 = sum of d_i * d_i in the same order; rstd = 1 / sqrt(S2 / H + eps)
-    if (tid < nr) {
-        const float* row = blk + tid * ld_h;
-        float s2 = 0.0f;
-        for (int64_t c = 0; c < H64; c += 64) {
-            f32x4 v[16];
-#pragma unroll
-            for (int q = 0; q < 16; ++q) v[q] = *reinterpret_cast<const f32x4*>(row + c + 4 * q);
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                const f32x4 sq = v[q] * v[q];
-                s2 = s2 + sq.x;
-                s2 = s2 + sq.y;
-                s2 = s2 + sq.z;
-                s2 = s2 + sq.w;
-            }
-        }
-        for (int64_t c = H64; c < H; ++c) {
-            const float sq = row[c] * row[c];
-            s2 = s2 + sq;
-        }
-        const float var = s2 / fh;
-        const float ve = var + eps;
-        const float sd = __builtin_sqrtf(ve);
-        const float rs = 1.0f / sd;
-        rs_s[tid] = rs;
-        if (mean_out) mean_out[row0 + tid] = mu_s[tid];
-        if (rstd_out) rstd_out[row0 + tid] = rs;
-    }
-    __syncthreads();
-
-    // y_i = (d_i * rstd) * gamma_i + beta_i, every lane
-    for (int e = tid; e < total; e += kLnThreads) {
-        const int r = e / groups, gi = e - r * groups;
-        const LnVec<W> v = ln_get<W>(blk + r * ld_h + gi * W);
-        LnVec<W> g, b, o;
-        if (gamma) g = ln_get<W>(gamma + static_cast<int64_t>(gi) * W);
-        if (beta) b = ln_get<W>(beta + static_cast<int64_t>(gi) * W);
-        const float q = rs_s[r];
-#pragma unroll
-        for (int w = 0; w < W; ++w) {
-            float t = v.v[w] * q;
-            if (gamma) t = t * g.v[w];
-            if (beta) t = t + b.v[w];
-            o.v[w] = t;
-        }
-        ln_put<W>(y + (row0 + r) * y_rs + static_cast<int64_t>(gi) * W, o);
-    }
-}
-
-// Lane 4q + g of the result holds lane 4q + (g + 3) % 4 of s: one step of a
-// ring around each quad (DPP quad permutation [3, 0, 1, 2]).
-__device__ __forceinline__ float quad_ring_step(float s) {
+// One step of a ring around each group of L lanes (L = 4 or 16): lane
+// g of a group receives lane (g - 1) mod L's s.  DPP quad permutation
+// [3, 0, 1, 2] for L = 4, row rotation by one for L = 16.
+template <int L>
+__device__ __forceinline__ float ring_step(float s) {
+    static_assert(L == 4 || L == 16, "ring of 4 or 16 lanes");
+    constexpr int kCtrl = L == 4 ? 0x93 : 0x121;
     return __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0x93, 0xF, 0xF, false));
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), kCtrl, 0xF, 0xF, false));
 }
 
-// Every lane of a quad receives lane 3's s (quad permutation [3, 3, 3, 3]).
-__device__ __forceinline__ float quad_from_last(float s) {
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0xFF, 0xF, 0xF, false));
+// Every lane of a group of L receives the group's last lane's s.
+template <int L>
+__device__ __forceinline__ float from_last(float s) {
+    if constexpr (L == 4)  // quad permutation [3, 3, 3, 3]
+        return __builtin_bit_cast(
+            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), 0xFF, 0xF, 0xF, false));
+    else
+        return __shfl(s, L - 1, L);
 }
 
-// The register-resident form, for rows of at most 4 * S elements.  A row
-// belongs to one quad of lanes (16 rows per wave) and is dealt out in pieces
-// of 8 elements: piece j of lane g is elements [32 j + 8 g, 32 j + 8 g + 8),
-// so that the quad reads and writes 128 contiguous bytes per piece.  Every
-// row is on chip at once and x is read once.
+// The register-resident form, for rows of at most L * S elements.  A row
+// belongs to a group of L consecutive lanes (64 / L rows per wave) and is
+// dealt out in pieces of P elements: piece j of lane g is elements
+// [j L P + g P, j L P + g P + P), so that the group reads and writes L P
+// contiguous floats per piece.  Every row is on chip at once and x is read
+// once.
 //
 // A fixed-order sum walks the pieces in row order, which visits the lanes of
-// the quad in turn: before each piece the running sums take one step around
-// the quad, so lane g receives the sum that lane g - 1 has just carried
-// through its piece, and adds its own 8 elements in ascending order.  All
-// four lanes run every step (three of them on values that the next steps
-// overwrite), so the adds that reach the result are exactly x_0, x_1, ...
-// in ascending order from +0.  The padding past H holds +0, which leaves a
-// running sum unchanged: it starts at +0 and so is never -0, and s + (+0) == s
-// for every other s (a NaN stays a NaN).
+// the group in turn: before each piece the running sums take one step around
+// the ring, so lane g receives the sum that lane g - 1 has just carried
+// through its piece, and adds its own P elements in ascending order.  All
+// lanes run every step (all but one on values that later steps overwrite),
+// so the adds that reach the result are exactly x_0, x_1, ... in ascending
+// order from +0.  The padding past H holds +0, which leaves a running sum
+// unchanged: it starts at +0 and so is never -0, and s + (+0) == s for every
+// other s (a NaN stays a NaN).
 //
-// FULL (16 live rows of exactly 4 * S elements) drops every bounds test, so
-// that the loads are unconditional and issued in piece order, and the sum
-// can start on the first piece while the later ones are still in flight.
-template <int S, bool VEC, bool FULL>
+// FULL (every row of the wave live and exactly L * S long) drops every
+// bounds test, so that the loads are unconditional and issued in piece order,
+// and the sum can start on the first piece while later ones are in flight.
+template <int L, int S, bool VEC, bool FULL>
 __device__ __forceinline__ void ln_regs_group(const float* xs, float* ys, int hl, bool live,
                                               int64_t row, int seg, float fh, float eps,
                                               const float* gs, const float* bs,
                                               float* __restrict__ mean_out,
                                               float* __restrict__ rstd_out) {
-    constexpr int kPieces = S / 8;
+    constexpr int P = L == 4 ? 8 : 4;  // elements per piece
+    constexpr int kPieces = S / P;
+    constexpr int kStride = L * P;     // row offset from one piece of a lane to its next
     float v[S];
     if constexpr (VEC) {
 #pragma unroll
         for (int q = 0; q < S / 4; ++q) {
-            const int o = 32 * (q >> 1) + 4 * (q & 1);
+            const int o = kStride * (q / (P / 4)) + 4 * (q % (P / 4));
             f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
             if (FULL || o < hl) a = *reinterpret_cast<const f32x4*>(xs + o);
             v[4 * q] = a.x;
@@ -575,7 +456,7 @@ __device__ __forceinline__ void ln_regs_group(const float* xs, float* ys, int hl
     } else {
 #pragma unroll
         for (int i = 0; i < S; ++i) {
-            const int o = 32 * (i >> 3) + (i & 7);
+            const int o = kStride * (i / P) + i % P;
             v[i] = (FULL || o < hl) ? xs[o] : 0.0f;
         }
     }
@@ -585,35 +466,35 @@ __device__ __forceinline__ void ln_regs_group(const float* xs, float* ys, int hl
 #pragma unroll
     for (int j = 0; j < kPieces; ++j) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            s = quad_ring_step(s);
+        for (int g = 0; g < L; ++g) {
+            s = ring_step<L>(s);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) s = s + v[8 * j + k];
+            for (int k = 0; k < P; ++k) s = s + v[P * j + k];
         }
     }
-    s = quad_from_last(s);
+    s = from_last<L>(s);
     const float mu = s / fh;
 
     // d_i = x_i - mu in place (+0 in the padding); S2 = sum of d_i * d_i
 #pragma unroll
     for (int i = 0; i < S; ++i) {
-        const int o = 32 * (i >> 3) + (i & 7);
+        const int o = kStride * (i / P) + i % P;
         v[i] = (FULL || o < hl) ? v[i] - mu : 0.0f;
     }
     float s2 = 0.0f;
 #pragma unroll
     for (int j = 0; j < kPieces; ++j) {
-        float sq[8];
+        float sq[P];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) sq[k] = v[8 * j + k] * v[8 * j + k];
+        for (int k = 0; k < P; ++k) sq[k] = v[P * j + k] * v[P * j + k];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            s2 = quad_ring_step(s2);
+        for (int g = 0; g < L; ++g) {
+            s2 = ring_step<L>(s2);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) s2 = s2 + sq[k];
+            for (int k = 0; k < P; ++k) s2 = s2 + sq[k];
         }
     }
-    s2 = quad_from_last(s2);
+    s2 = from_last<L>(s2);
     const float var = s2 / fh;
     const float ve = var + eps;
     const float sd = __builtin_sqrtf(ve);
@@ -627,7 +508,7 @@ __device__ __forceinline__ void ln_regs_group(const float* xs, float* ys, int hl
     if constexpr (VEC) {
 #pragma unroll
         for (int q = 0; q < S / 4; ++q) {
-            const int o = 32 * (q >> 1) + 4 * (q & 1);
+            const int o = kStride * (q / (P / 4)) + 4 * (q % (P / 4));
             if (FULL || o < hl) {
                 f32x4 t;
                 t.x = v[4 * q] * rs;
@@ -642,7 +523,7 @@ __device__ __forceinline__ void ln_regs_group(const float* xs, float* ys, int hl
     } else {
 #pragma unroll
         for (int i = 0; i < S; ++i) {
-            const int o = 32 * (i >> 3) + (i & 7);
+            const int o = kStride * (i / P) + i % P;
             if (FULL || o < hl) {
                 float t = v[i] * rs;
                 t = t * gs[o];
@@ -653,24 +534,26 @@ __device__ __forceinline__ void ln_regs_group(const float* xs, float* ys, int hl
     }
 }
 
-template <int S, bool VEC>
+template <int L, int S, bool VEC>
 __global__ __launch_bounds__(64) void repops_layernorm_regs_kernel(
     const float* x, int64_t x_rs, const float* __restrict__ gamma,
     const float* __restrict__ beta, float* y, int64_t y_rs, int64_t rows, int64_t H, float eps,
     float* __restrict__ mean_out, float* __restrict__ rstd_out) {
+    constexpr int P = L == 4 ? 8 : 4;
+    constexpr int R = 64 / L;  // rows per wave
     // gamma and beta, staged once per workgroup.  A missing gamma is staged
     // as 1 and a missing beta as -0: t * 1 == t and t + (-0) == t for every
     // binary32 t (signed zeros, infinities and NaN included), so the output
     // step needs no branch and matches skipping the operation.
-    __shared__ __align__(16) float ln_g[4 * S];
-    __shared__ __align__(16) float ln_b[4 * S];
+    __shared__ __align__(16) float ln_g[L * S];
+    __shared__ __align__(16) float ln_b[L * S];
     const int lane = static_cast<int>(threadIdx.x);
-    const int seg = lane & 3;
-    const int64_t groups = (rows + 15) / 16;
+    const int seg = lane % L;
+    const int64_t groups = (rows + R - 1) / R;
     const float fh = static_cast<float>(H);
     const int hi = static_cast<int>(H);
     if constexpr (VEC) {
-        for (int c = 4 * lane; c < 4 * S; c += 256) {
+        for (int c = 4 * lane; c < L * S; c += 256) {
             f32x4 gv = {1.0f, 1.0f, 1.0f, 1.0f}, bv = {-0.0f, -0.0f, -0.0f, -0.0f};
             if (gamma && c < hi) gv = *reinterpret_cast<const f32x4*>(gamma + c);
             if (beta && c < hi) bv = *reinterpret_cast<const f32x4*>(beta + c);
@@ -678,27 +561,27 @@ __global__ __launch_bounds__(64) void repops_layernorm_regs_kernel(
             *reinterpret_cast<f32x4*>(ln_b + c) = bv;
         }
     } else {
-        for (int c = lane; c < 4 * S; c += 64) {
+        for (int c = lane; c < L * S; c += 64) {
             ln_g[c] = gamma && c < hi ? gamma[c] : 1.0f;
             ln_b[c] = beta && c < hi ? beta[c] : -0.0f;
         }
     }
     __syncthreads();
     for (int64_t rg = blockIdx.x; rg < groups; rg += gridDim.x) {
-        const int64_t row = rg * 16 + (lane >> 2);
+        const int64_t row = rg * R + lane / L;
         const bool live = row < rows;
-        // element 32 j + 8 seg + k of the row is at offset o = 32 j + k from
+        // element j L P + seg P + k of the row is at offset o = j L P + k from
         // xs, and exists when o < hl
-        const int hl = live ? hi - 8 * seg : 0;
-        const float* xs = x + (live ? row : 0) * x_rs + 8 * seg;
-        float* ys = y + (live ? row : 0) * y_rs + 8 * seg;
-        const bool full = (rg + 1) * 16 <= rows && hi == 4 * S;
+        const int hl = live ? hi - P * seg : 0;
+        const float* xs = x + (live ? row : 0) * x_rs + P * seg;
+        float* ys = y + (live ? row : 0) * y_rs + P * seg;
+        const bool full = (rg + 1) * R <= rows && hi == L * S;
         if (full)
-            ln_regs_group<S, VEC, true>(xs, ys, hl, live, row, seg, fh, eps, ln_g + 8 * seg,
-                                        ln_b + 8 * seg, mean_out, rstd_out);
+            ln_regs_group<L, S, VEC, true>(xs, ys, hl, live, row, seg, fh, eps, ln_g + P * seg,
+                                           ln_b + P * seg, mean_out, rstd_out);
         else
-            ln_regs_group<S, VEC, false>(xs, ys, hl, live, row, seg, fh, eps, ln_g + 8 * seg,
-                                         ln_b + 8 * seg, mean_out, rstd_out);
+            ln_regs_group<L, S, VEC, false>(xs, ys, hl, live, row, seg, fh, eps, ln_g + P * seg,
+                                            ln_b + P * seg, mean_out, rstd_out);
     }
 }
 
@@ -723,38 +606,50 @@ int launch_layernorm(const float* x, int64_t x_rs, const float* gamma, const flo
                      int64_t y_rs, int64_t rows, int64_t H, float eps, float* mean, float* rstd,
                      bool vec, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // Register-resident form for rows of at most 768 elements (the row and
-    // its squared deviations are both held: 2 * 192 registers per lane).
-    if (H <= 768) {
+    // Register-resident forms for rows of at most 4096 elements: a quad of
+    // lanes per row up to 768 (16 rows per wave), 16 lanes per row above
+    // (4 rows per wave).  S (elements per lane) is the smallest that holds
+    // the row, since every sum walks all L * S slots.
+    if (H <= 4096) {
         using Gn = void (*)(const float*, int64_t, const float*, const float*, float*, int64_t,
                             int64_t, int64_t, float, float*, float*);
         Gn gn;
-        if (H <= 256)
-            gn = vec ? repops_layernorm_regs_kernel<64, true> : repops_layernorm_regs_kernel<64, false>;
-        else if (H <= 512)
-            gn = vec ? repops_layernorm_regs_kernel<128, true> : repops_layernorm_regs_kernel<128, false>;
-        else
-            gn = vec ? repops_layernorm_regs_kernel<192, true> : repops_layernorm_regs_kernel<192, false>;
-        const int64_t groups = (rows + 15) / 16;
+        int rows_per_wave = 4;
+        if (H <= 256) {
+            gn = vec ? repops_layernorm_regs_kernel<4, 64, true>
+                     : repops_layernorm_regs_kernel<4, 64, false>;
+            rows_per_wave = 16;
+        } else if (H <= 512) {
+            gn = vec ? repops_layernorm_regs_kernel<4, 128, true>
+                     : repops_layernorm_regs_kernel<4, 128, false>;
+            rows_per_wave = 16;
+        } else if (H <= 768) {
+            gn = vec ? repops_layernorm_regs_kernel<4, 192, true>
+                     : repops_layernorm_regs_kernel<4, 192, false>;
+            rows_per_wave = 16;
+        } else if (H <= 1024) {
+            gn = vec ? repops_layernorm_regs_kernel<16, 64, true>
+                     : repops_layernorm_regs_kernel<16, 64, false>;
+        } else if (H <= 1536) {
+            gn = vec ? repops_layernorm_regs_kernel<16, 96, true>
+                     : repops_layernorm_regs_kernel<16, 96, false>;
+        } else if (H <= 2048) {
+            gn = vec ? repops_layernorm_regs_kernel<16, 128, true>
+                     : repops_layernorm_regs_kernel<16, 128, false>;
+        } else if (H <= 3072) {
+            gn = vec ? repops_layernorm_regs_kernel<16, 192, true>
+                     : repops_layernorm_regs_kernel<16, 192, false>;
+        } else {
+            gn = vec ? repops_layernorm_regs_kernel<16, 256, true>
+                     : repops_layernorm_regs_kernel<16, 256, false>;
+        }
+        const int64_t groups = (rows + rows_per_wave - 1) / rows_per_wave;
         const int64_t gblocks = groups < (int64_t(1) << 20) ? groups : (int64_t(1) << 20);
         hipLaunchKernelGGL(gn, dim3(static_cast<unsigned>(gblocks)), dim3(64), 0, s, x, x_rs,
                            gamma, beta, y, y_rs, rows, H, eps, mean, rstd);
         return static_cast<int>(hipGetLastError());
     }
-    // Resident form when a block of kLnResRows rows fits in 32 KB of LDS.
-    const int64_t ld_h = ((H + 3) & ~int64_t(3)) + 4;
-    const int64_t lds = kLnResRows * ld_h * 4;
-    if (lds <= 32768) {
-        using Rn = void (*)(const float*, int64_t, const float*, const float*, float*, int64_t,
-                            int64_t, int64_t, int, float, float*, float*);
-        Rn rn = vec ? repops_layernorm_resident_kernel<true>
-                    : repops_layernorm_resident_kernel<false>;
-        const int64_t rblocks = (rows + kLnResRows - 1) / kLnResRows;
-        hipLaunchKernelGGL(rn, dim3(static_cast<unsigned>(rblocks)), dim3(kLnThreads),
-                           static_cast<unsigned>(lds), s, x, x_rs, gamma, beta, y, y_rs, rows, H,
-                           static_cast<int>(ld_h), eps, mean, rstd);
-        return static_cast<int>(hipGetLastError());
-    }
+    // Longer rows stream through LDS.
     const int64_t blocks = (rows + kLnRows - 1) / kLnRows;
     using Fn = void (*)(const float*, int64_t, const float*, const float*, float*, int64_t,
                         int64_t, int64_t, float, float*, float*);

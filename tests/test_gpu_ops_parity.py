@@ -5,8 +5,8 @@ repops_layernorm_f32 through the C ABI) against the CPU oracle, bit for bit
 Covered: hand-picked and random inputs with tiny, subnormal, huge and special
 values; a sweep of 2^24 bit patterns spread over every exponent; lengths 0 to
 2^20 + 3 on the 16-byte and the element-wise paths; in-place calls;
-LayerNorm for H from 1 to 4096 and 1 to 4099 rows, with and without gamma and
-beta, strided and misaligned rows, in place, rows whose variance is subnormal
+LayerNorm for H from 1 to 4097 (both sides of every kernel form's limit) and
+1 to 4099 rows, with and without gamma and beta, strided and misaligned rows, in place, rows whose variance is subnormal
 or zero and rows holding infinities and NaN; and the full DistilBERT-shaped
 workloads the benchmark times, compared in full."""
 from __future__ import annotations
@@ -158,8 +158,9 @@ def check_layernorm(x, gamma, beta, eps, **kw):
 
 @pytest.mark.parametrize("rows,H", [(1, 1), (3, 2), (5, 3), (64, 4), (65, 5), (17, 63),
                                     (31, 256), (16, 257), (33, 512), (47, 513), (63, 768),
-                                    (18, 767), (19, 769), (130, 1023), (7, 2044), (9, 2045),
-                                    (7, 4096), (4099, 8)])
+                                    (18, 767), (19, 769), (130, 1023), (5, 1024), (6, 1025),
+                                    (7, 1536), (9, 1537), (7, 2044), (9, 2048), (10, 2049),
+                                    (5, 3072), (6, 3073), (7, 4096), (3, 4097), (4099, 8)])
 def test_layernorm_shapes(rows, H):
     say("layernorm rows=%d H=%d" % (rows, H))
     rng = np.random.default_rng(rows * 31 + H)
