@@ -108,9 +108,9 @@ int launch_fold(const FoldArgs& G, int n, bool first, bool last, float* sum, flo
 
 // Tensor hash (repops_merkle.hip): SHA-256 Merkle root of total_words 32-bit
 // words cut into leaves of leaf_words.  The root is written as the digest's
-// 32 bytes; `ws` holds merkle_workspace_bytes(n_leaves) bytes.  vec: data is
-// 16-byte aligned and leaf_words is a multiple of 4.
-int64_t merkle_workspace_bytes(int64_t n_leaves);
+// 32 bytes; `ws` holds merkle_workspace_bytes(n_leaves, leaf_words) bytes.
+// vec: data is 16-byte aligned and leaf_words is a multiple of 4.
+int64_t merkle_workspace_bytes(int64_t n_leaves, int64_t leaf_words);
 int launch_merkle_root(const uint32_t* data, int64_t total_words, int64_t leaf_words, void* ws,
                        uint32_t* root, bool vec, void* stream);
 // match[c] = (claims[8c .. 8c+7] == root[0 .. 7]) for c < nclaims.

@@ -15,19 +15,20 @@
 //
 // One lane hashes one leaf (SHA-256 is a serial chain of compressions; the
 // leaves are the parallel dimension).  A workgroup of kLeafGroup lanes then
-// folds its neighbouring leaf digests up the tree in LDS, so the first launch
-// turns n leaves into ceil(n / 256) digests; each later launch folds groups of
-// kNodeGroup digests the same way, until one is left.  Groups start at
-// multiples of their (power-of-two) size, so a group's fold is exactly a
-// subtree of the global tree.  At every level the pairs are packed into the
-// lowest lanes, so a level with p pairs keeps ceil(p / 64) waves busy rather
-// than touching every wave of the group.
+// folds its neighbouring leaf digests a few levels up the tree in LDS (none
+// for long leaves; all the way to the root when it is the only workgroup) and
+// writes the subtree roots; each later launch folds groups of kNodeGroup
+// digests to one, until one is left.  Groups start at multiples of their
+// (power-of-two) size and every level pairs neighbours, so each fold is
+// exactly a piece of the global tree.  At every level the pairs are packed
+// into the lowest lanes, so a level with p pairs keeps ceil(p / 64) waves busy
+// rather than touching every wave of the group.
 //
 // Costs on gfx950: a funnel shift (the rotate) and a three-input add issue at
 // half the rate of a plain add, xor or three-input logic op, and one wave
 // alone gets half of its SIMD's issue rate.  The leaves run at about 3.5
-// waves per SIMD for a 235 MB tensor; the top of the tree is a chain of two
-// compressions per level on one lane.
+// waves per SIMD for a 235 MB tensor in 1 KiB leaves; the top of the tree is
+// a chain of two compressions per level on one lane.
 //
 // Everything is 32-bit integer arithmetic; there is no floating point here.
 #include <hip/hip_runtime.h>
@@ -38,6 +39,17 @@ namespace repops {
 namespace {
 
 constexpr int kLeafGroup = 256;   // lanes (and leaves) per workgroup, first launch
+// How many tree levels the first launch folds before writing its digests
+// (when it is not the last launch).  Its fold levels run with few lanes busy;
+// that is hidden only behind later workgroups' leaves, so long leaves (one
+// generation of workgroups at realistic sizes) fold nothing and short ones
+// fold 2 levels.  Tiny leaves fold until 256 bytes of data sit under each
+// digest, which keeps the workspace (the digests) at most 1/8 of the data.
+// Measured on a 235 MB tensor: 64 B leaves 839 us with 2 levels (911 with 4);
+// 256 B 373 us with 2 (501 with 0, 418 with 4); 1 KiB 300 us with 0 (314 with
+// 1, 345 with 8).
+constexpr int64_t kLongLeafBytes = 1024;
+constexpr int64_t kMinSpanBytes = 256;
 constexpr int kNodeGroup = 1024;  // lanes (and digests) per workgroup, later launches
 
 // FIPS 180-4, section 4.2.2: the first 32 bits of the fractional parts of
@@ -220,10 +232,12 @@ __host__ __device__ __forceinline__ void hash_node(const uint32_t (&l)[8], const
 // src[8i .. 8i+7].  A workgroup of G lanes takes G consecutive items and
 // writes the root of their subtree to dst[8*blockIdx.x ..]; FINAL (a single
 // workgroup): the root of the whole tree, as the digest's 32 bytes.
+constexpr int log2_of(int g) { return g <= 1 ? 0 : 1 + log2_of(g / 2); }
+
 template <int G, bool LEAF, bool VEC, bool FINAL>
 __global__ __launch_bounds__(G) void repops_merkle_kernel(const uint32_t* __restrict__ src,
                                                           int64_t n_items, int64_t leaf_words,
-                                                          int64_t total_words,
+                                                          int64_t total_words, int levels,
                                                           uint32_t* __restrict__ dst) {
     // Two node buffers: level l reads one and writes the other, so one
     // barrier per level separates every write from the reads before it.
@@ -251,7 +265,8 @@ __global__ __launch_bounds__(G) void repops_merkle_kernel(const uint32_t* __rest
     // hashes the pair (2p, 2p+1) into slot p of the other buffer; with n odd,
     // lane n/2 carries the last node up unchanged.  Lane 0 ends with the root.
     int cur = 0;
-    for (int n = count; n > 1; n = (n + 1) >> 1) {
+    int n = count;
+    for (int lv = 0; n > 1 && lv < levels; n = (n + 1) >> 1, ++lv) {
         __syncthreads();
         const int pairs = n >> 1;
         if (tid < pairs) {
@@ -273,10 +288,21 @@ __global__ __launch_bounds__(G) void repops_merkle_kernel(const uint32_t* __rest
         }
         cur ^= 1;
     }
-    if (tid == 0) {
-        uint32_t* o = dst + static_cast<int64_t>(blockIdx.x) * 8;
+    if (levels >= log2_of(G)) {
+        if (tid == 0) {
+            uint32_t* o = dst + static_cast<int64_t>(blockIdx.x) * 8;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) o[q] = FINAL ? bswap32(h[q]) : h[q];
+            for (int q = 0; q < 8; ++q) o[q] = FINAL ? bswap32(h[q]) : h[q];
+        }
+    } else {
+        // n subtree roots of 2^levels items each (the last one possibly
+        // smaller) sit in slots 0..n-1
+        __syncthreads();
+        if (tid < n) {
+            uint32_t* o = dst + (static_cast<int64_t>(blockIdx.x) * (G >> levels) + tid) * 8;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) o[q] = node[cur][q][tid];
+        }
     }
 }
 
@@ -313,12 +339,19 @@ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 }  // namespace
 
-int64_t merkle_workspace_bytes(int64_t n_leaves) {
+int merkle_fold_levels(int64_t leaf_words) {
+    if (leaf_words * 4 >= kLongLeafBytes) return 0;
+    int levels = 2;
+    while (levels < log2_of(kLeafGroup) && (leaf_words * 4 << levels) < kMinSpanBytes) ++levels;
+    return levels;
+}
+
+int64_t merkle_workspace_bytes(int64_t n_leaves, int64_t leaf_words) {
     // Two ping-pong buffers: the first launch's digests and the second's;
     // later launches alternate between them (each is consumed before it is
     // refilled, in stream order).
     if (n_leaves <= kLeafGroup) return 0;
-    const int64_t n1 = ceil_div(n_leaves, kLeafGroup);
+    const int64_t n1 = ceil_div(n_leaves, int64_t(1) << merkle_fold_levels(leaf_words));
     const int64_t n2 = ceil_div(n1, kNodeGroup);
     return round_up(n1 * 32, 256) + (n2 > 1 ? round_up(n2 * 32, 256) : 0);
 }
@@ -331,30 +364,43 @@ int launch_merkle_root(const uint32_t* data, int64_t total_words, int64_t leaf_w
         return static_cast<int>(hipGetLastError());
     }
     const int64_t n_leaves = ceil_div(total_words, leaf_words);
-    const int64_t n1 = ceil_div(n_leaves, kLeafGroup);
-    uint32_t* buf[2] = {static_cast<uint32_t*>(ws), nullptr};
-    if (n1 > 1) buf[1] = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + round_up(n1 * 32, 256));
-
-    using Fn = void (*)(const uint32_t*, int64_t, int64_t, int64_t, uint32_t*);
-    int64_t n = n_leaves;
-    const uint32_t* src = data;
-    for (int stage = 0;; ++stage) {
-        const int group = stage == 0 ? kLeafGroup : kNodeGroup;
-        const int64_t blocks = ceil_div(n, group);
+    using Fn = void (*)(const uint32_t*, int64_t, int64_t, int64_t, int, uint32_t*);
+    hipError_t err;
+    if (n_leaves <= kLeafGroup) {
+        // one workgroup folds every leaf into the root
+        Fn f = vec ? repops_merkle_kernel<kLeafGroup, true, true, true>
+                   : repops_merkle_kernel<kLeafGroup, true, false, true>;
+        hipLaunchKernelGGL(f, dim3(1), dim3(kLeafGroup), 0, s, data, n_leaves, leaf_words,
+                           total_words, log2_of(kLeafGroup), root);
+        return static_cast<int>(hipGetLastError());
+    }
+    // First launch: the leaves, folded `levels` levels, into n1 digests.
+    const int levels = merkle_fold_levels(leaf_words);
+    const int64_t n1 = ceil_div(n_leaves, int64_t(1) << levels);
+    uint32_t* buf[2] = {static_cast<uint32_t*>(ws),
+                        reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + round_up(n1 * 32, 256))};
+    {
+        Fn f = vec ? repops_merkle_kernel<kLeafGroup, true, true, false>
+                   : repops_merkle_kernel<kLeafGroup, true, false, false>;
+        hipLaunchKernelGGL(f, dim3(static_cast<unsigned>(ceil_div(n_leaves, kLeafGroup))),
+                           dim3(kLeafGroup), 0, s, data, n_leaves, leaf_words, total_words, levels,
+                           buf[0]);
+        err = hipGetLastError();
+        if (err != hipSuccess) return static_cast<int>(err);
+    }
+    // Later launches: groups of kNodeGroup digests folded to one each, until
+    // one launch writes the root.
+    int64_t n = n1;
+    const uint32_t* src = buf[0];
+    for (int stage = 1;; ++stage) {
+        const int64_t blocks = ceil_div(n, kNodeGroup);
         const bool final_stage = blocks == 1;
         uint32_t* dst = final_stage ? root : buf[stage & 1];
-        Fn fn;
-        if (stage == 0)
-            fn = final_stage ? (vec ? repops_merkle_kernel<kLeafGroup, true, true, true>
-                                    : repops_merkle_kernel<kLeafGroup, true, false, true>)
-                             : (vec ? repops_merkle_kernel<kLeafGroup, true, true, false>
-                                    : repops_merkle_kernel<kLeafGroup, true, false, false>);
-        else
-            fn = final_stage ? repops_merkle_kernel<kNodeGroup, false, false, true>
-                             : repops_merkle_kernel<kNodeGroup, false, false, false>;
-        hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(group), 0, s, src, n,
-                           leaf_words, total_words, dst);
-        const hipError_t err = hipGetLastError();
+        Fn fn = final_stage ? repops_merkle_kernel<kNodeGroup, false, false, true>
+                            : repops_merkle_kernel<kNodeGroup, false, false, false>;
+        hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(kNodeGroup), 0, s, src, n,
+                           int64_t(0), int64_t(0), log2_of(kNodeGroup), dst);
+        err = hipGetLastError();
         if (err != hipSuccess) return static_cast<int>(err);
         if (final_stage) return 0;
         src = dst;

@@ -24,7 +24,7 @@ bool sizes_ok(int64_t nbytes, int64_t leaf_bytes) {
 
 int64_t workspace_for(int64_t nbytes, int64_t leaf_bytes) {
     if (nbytes == 0) return 0;
-    return merkle_workspace_bytes((nbytes + leaf_bytes - 1) / leaf_bytes);
+    return merkle_workspace_bytes((nbytes + leaf_bytes - 1) / leaf_bytes, leaf_bytes / 4);
 }
 
 bool span_overlap(const void* p, int64_t np, const void* q, int64_t nq) {

@@ -226,8 +226,10 @@ repops_status repops_fold_mean_sgd_f32(const float* const* grads, int64_t k, int
 /*
  * Bytes of device workspace repops_merkle_root needs for nbytes of data in
  * leaves of leaf_bytes (0 when the tree fits one workgroup, i.e. at most 256
- * leaves), or -1 when the sizes are invalid (see repops_merkle_root).  Host
- * only; touches no device.
+ * leaves), or -1 when the sizes are invalid (see repops_merkle_root).  It
+ * holds intermediate digests: 32 bytes per leaf for leaves of 1 KiB or more,
+ * at most nbytes / 8 for shorter ones, plus under 1 %.  Host only; touches
+ * no device.
  */
 int64_t repops_merkle_workspace_bytes(int64_t nbytes, int64_t leaf_bytes);
 

@@ -66,17 +66,21 @@ def test_workspace_query():
     ws = rp.repops_merkle_workspace_bytes
     assert ws(0, 1024) == 0
     assert ws(256 * 1024, 1024) == 0            # 256 leaves: one workgroup
-    assert ws(256 * 1024 + 4, 1024) == 256      # 257 leaves: two digests
-    assert ws(4096 * 14336 * 4, 1024) == 28672    # 896 digests, then one group
-    assert ws(4 * (256 * 1024 + 1), 4) == 33024 + 256  # 1025 digests, then 2
+    # Leaves of 256 bytes or more: the first launch writes one digest per
+    # leaf; shorter leaves are folded until 256 bytes sit under each digest.
+    assert ws(256 * 1024 + 4, 1024) == 8448     # 257 digests (8224 B, rounded to 256)
+    assert ws(4096 * 14336 * 4, 1024) == 7340032 + 7168   # 229376 digests, then 224
+    assert ws(4 * (256 * 1024 + 1), 4) == 131328 + 256    # 4-byte leaves, 64 per digest:
+    #                                                        4097 digests, then 5
+    assert ws(256 * 1024 + 64, 64) == 33024 + 256  # 64-byte leaves, 4 per digest: 1025, then 2
     for nbytes, leaf in ((6, 4), (-4, 4), (8, 6), (8, 0), (8, 2), (8, (1 << 24) + 4),
                          ((1 << 50) + 4, 1024)):
         assert ws(nbytes, leaf) == -1, (nbytes, leaf)
 
 
 def root_call(**kw):
-    # 1 MiB in 1 KiB leaves: 4 digests after the first stage, 256 bytes of
-    # workspace.  Every call made with this helper is invalid in one way.
+    # 1 MiB in 1 KiB leaves: 1024 digests after the first stage, 32768 bytes
+    # of workspace.  Every call made with this helper is invalid in one way.
     args = dict(data=PD, nbytes=1 << 20, leaf_bytes=1024, workspace=PW, workspace_bytes=1 << 16,
                 root=PR, stream=0)
     args.update(kw)
@@ -93,16 +97,17 @@ def test_merkle_root_argument_errors():
     assert root_call(data=PD + 2) == rp.REPOPS_ERR_ALIGN
     assert root_call(workspace=PW + 4) == rp.REPOPS_ERR_ALIGN
     assert root_call(workspace=None) == rp.REPOPS_ERR_WORKSPACE
-    assert root_call(workspace_bytes=255) == rp.REPOPS_ERR_WORKSPACE  # 256 needed
+    assert root_call(workspace_bytes=32767) == rp.REPOPS_ERR_WORKSPACE  # 32768 needed
     assert root_call(root=PD + 1024) == rp.REPOPS_ERR_ALIAS
     assert root_call(workspace=PD + 4096) == rp.REPOPS_ERR_ALIAS
     assert root_call(root=PW + 32) == rp.REPOPS_ERR_ALIAS
 
 
 def referee_call(**kw):
-    # 1024 x 512 outputs = 2048 leaves of 1 KiB: a 256-byte workspace is needed
+    # 1024 x 512 outputs = 2048 leaves of 1 KiB: 65536 + 256 bytes of
+    # workspace are needed
     args = dict(A=PA, a_rs=64, a_cs=1, B=PB, b_rs=512, b_cs=1, C=PC, M=1024, N=512, K=64,
-                trans_a=0, trans_b=0, leaf_bytes=1024, workspace=PW, workspace_bytes=4096,
+                trans_a=0, trans_b=0, leaf_bytes=1024, workspace=PW, workspace_bytes=65792,
                 claims=PCL, nclaims=2, root=PR, match=PM, stream=0)
     args.update(kw)
     return rp.repops_referee_matmul_f32(**args)
@@ -118,6 +123,7 @@ def test_referee_argument_errors():
     assert referee_call(match=None) == rp.REPOPS_ERR_NULL
     assert referee_call(match=PM + 2) == rp.REPOPS_ERR_ALIGN
     assert referee_call(workspace_bytes=0) == rp.REPOPS_ERR_WORKSPACE
+    assert referee_call(workspace_bytes=65791) == rp.REPOPS_ERR_WORKSPACE
     assert referee_call(match=PC + 64) == rp.REPOPS_ERR_ALIAS
     assert referee_call(claims=PC) == rp.REPOPS_ERR_ALIAS
     assert referee_call(root=PC + 32) == rp.REPOPS_ERR_ALIAS
