@@ -173,28 +173,31 @@ def test_layernorm_shapes(rows, H):
     check_layernorm(x, g, None, 0.5)
 
 
-@pytest.mark.parametrize("x_rs,offset", [(772, 0), (771, 0), (768, 1), (1000, 3)])
-def test_layernorm_strided_and_misaligned(x_rs, offset):
-    say("layernorm x_rs=%d offset=%d" % (x_rs, offset))
+@pytest.mark.parametrize("H,x_rs,offset", [(768, 772, 0), (768, 771, 0), (768, 768, 1),
+                                          (768, 1000, 3), (1024, 1030, 0), (1024, 1027, 2),
+                                          (2500, 2600, 0), (4096, 4100, 1)])
+def test_layernorm_strided_and_misaligned(H, x_rs, offset):
+    say("layernorm H=%d x_rs=%d offset=%d" % (H, x_rs, offset))
     rng = np.random.default_rng(x_rs + offset)
-    x = rng.standard_normal((70, 768)).astype(np.float32)
-    g = (1 + 0.1 * rng.standard_normal(768)).astype(np.float32)
-    b = (0.1 * rng.standard_normal(768)).astype(np.float32)
+    x = rng.standard_normal((70, H)).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(H)).astype(np.float32)
+    b = (0.1 * rng.standard_normal(H)).astype(np.float32)
     check_layernorm(x, g, b, 1e-12, x_rs=x_rs, offset=offset)
 
 
-def test_layernorm_in_place():
-    say("layernorm in place")
-    rng = np.random.default_rng(5)
-    x = rng.standard_normal((100, 96)).astype(np.float32)
-    g = rng.standard_normal(96).astype(np.float32)
-    b = rng.standard_normal(96).astype(np.float32)
+@pytest.mark.parametrize("H", [96, 1024, 3000])
+def test_layernorm_in_place(H):
+    say("layernorm in place H=%d" % H)
+    rng = np.random.default_rng(5 + H)
+    x = rng.standard_normal((37, H)).astype(np.float32)
+    g = rng.standard_normal(H).astype(np.float32)
+    b = rng.standard_normal(H).astype(np.float32)
     check_layernorm(x, g, b, 1e-5, in_place=True)
 
 
-def test_layernorm_extreme_rows():
-    say("layernorm extreme rows")
-    H = 33
+@pytest.mark.parametrize("H", [33, 1500])
+def test_layernorm_extreme_rows(H):
+    say("layernorm extreme rows H=%d" % H)
     rows = [np.full(H, 7.5), np.zeros(H), np.full(H, -0.0),
             np.linspace(-1e-30, 1e-30, H),           # subnormal variance
             np.linspace(-1e-21, 1e-21, H),
