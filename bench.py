@@ -148,17 +148,22 @@ def cpu_baseline(A, B, w, target_s):
 
 
 def main():
+    from bit_reproducible_fp32_amd import inputs
+
+    families = (("matmul", inputs.WORKLOADS), ("fold", inputs.FOLD_WORKLOADS),
+                ("batched matmul", inputs.BATCHED_WORKLOADS), ("tensor hash", inputs.HASH_WORKLOADS),
+                ("erf/GeLU/LayerNorm", inputs.OPS_WORKLOADS))
+    names = "; ".join("%s: %s" % (f, ", ".join(sorted(d))) for f, d in families)
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default 20 for a matmul, 100 for the sub-millisecond "
-                         "batched and fold steps)")
+                    help="timed steps (default 20 for a matmul workload, 100 for the others, "
+                         "whose steps take well under a millisecond)")
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed steps before timing (default 5 for a matmul, 200 for the "
-                         "batched and fold steps, enough for the clock to settle)")
+                    help="untimed steps before timing (default 5 for a matmul workload, 200 "
+                         "for the others, enough for the clock to settle)")
     ap.add_argument("--workload", default="llama8b_mlp_up",
-                    help="a matmul workload (default: the Llama-8B up-projection) or a "
-                         "fold workload (fixed-order gradient average + SGD step)")
+                    help="the workload to time (default: the Llama-8B up-projection). " + names)
     ap.add_argument("--variant", default=None, help="force a kernel variant (name or index)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -166,7 +171,8 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
-    from bit_reproducible_fp32_amd import inputs
+    if not any(args.workload in d for _, d in families):
+        ap.error("unknown workload %r; known: %s" % (args.workload, names))
 
     short = args.workload not in inputs.WORKLOADS
     if args.steps is None:
