@@ -416,8 +416,8 @@ __device__ __forceinline__ float from_last(float s) {
 // belongs to a group of L consecutive lanes (64 / L rows per wave) and is
 // dealt out in pieces of P elements: piece j of lane g is elements
 // [j L P + g P, j L P + g P + P), so that the group reads and writes L P
-// contiguous floats per piece.  Every row is on chip at once and x is read
-// once.
+// contiguous floats per piece.  A wave keeps its rows in registers from load
+// to output, so x is read once.
 //
 // A fixed-order sum walks the pieces in row order, which visits the lanes of
 // the group in turn: before each piece the running sums take one step around
