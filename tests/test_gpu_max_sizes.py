@@ -1,8 +1,9 @@
 """GPU parity at the largest sizes the entry points are built for: an output
 with more than 2^31 elements (64-bit offsets in every kernel's epilogue),
-a very long fixed-order sum (K = 2^17 + 3), and a LayerNorm row of 2^20 + 5
-elements, all against the CPU oracle bit for bit (the huge output on
-sampled entries, read back on the device)."""
+a very long fixed-order sum (K = 2^17 + 3), a LayerNorm row of 2^20 + 5
+elements, and LayerNorm launches with more row groups than workgroups, all
+against the CPU oracle bit for bit (the huge outputs on sampled entries,
+read back on the device)."""
 from __future__ import annotations
 
 import numpy as np
@@ -88,3 +89,29 @@ def test_layernorm_long_row():
     same_bits(y.cpu().numpy(), want[0], "y")
     same_bits(mean.cpu().numpy(), want[1], "mean")
     same_bits(rstd.cpu().numpy(), want[2], "rstd")
+
+
+@pytest.mark.parametrize("rows,H", [((1 << 24) + 5, 8), ((1 << 22) + 3, 776)])
+def test_layernorm_more_row_groups_than_workgroups(rows, H):
+    """More row groups than the 2^20 workgroups a register-form launch uses
+    (16 rows per group at H = 8, 4 at H = 776), so workgroups take a second
+    group; sampled rows (first, last, around the wrap) against the oracle."""
+    say("LayerNorm rows=%d H=%d (grid-stride)" % (rows, H))
+    gen = torch.Generator(device=DEV).manual_seed(91 + H)
+    x = torch.randn(rows, H, device=DEV, generator=gen) * 2 + 0.25
+    g = torch.from_numpy(inputs.random_matrix((H,), 92)).to(DEV)
+    b = torch.from_numpy(inputs.random_matrix((H,), 93)).to(DEV)
+    y, mean, rstd = rp.layernorm(x, g, b, 1e-5, return_stats=True)
+    per = 16 if H <= 768 else 4
+    wrap = (1 << 20) * per
+    pick = np.unique(np.r_[0, 1, per - 1, per, wrap - 1, wrap, wrap + 1, rows - per - 1,
+                           rows - 2, rows - 1,
+                           np.random.default_rng(94).integers(0, rows, 48)])
+    it = torch.from_numpy(pick).to(DEV)
+    xs = x[it].cpu().numpy()
+    want = oracle.layernorm_f32(xs, g.cpu().numpy(), b.cpu().numpy(), 1e-5)
+    same_bits(y[it].cpu().numpy(), want[0], "y")
+    same_bits(mean[it].cpu().numpy(), want[1], "mean")
+    same_bits(rstd[it].cpu().numpy(), want[2], "rstd")
+    del x, y
+    torch.cuda.empty_cache()
