@@ -5,7 +5,7 @@ repops_layernorm_f32 through the C ABI) against the CPU oracle, bit for bit
 Covered: hand-picked and random inputs with tiny, subnormal, huge and special
 values; a sweep of 2^24 bit patterns spread over every exponent; lengths 0 to
 2^20 + 3 on the 16-byte and the element-wise paths; in-place calls;
-LayerNorm for H from 1 to 4097 (both sides of every kernel form's limit) and
+LayerNorm for H from 1 to 8193 (both sides of every kernel form's limit) and
 1 to 4099 rows, with and without gamma and beta, strided and misaligned rows, in place, rows whose variance is subnormal
 or zero and rows holding infinities and NaN; and the full DistilBERT-shaped
 workloads the benchmark times, compared in full."""
@@ -160,7 +160,8 @@ def check_layernorm(x, gamma, beta, eps, **kw):
                                     (31, 256), (16, 257), (33, 512), (47, 513), (63, 768),
                                     (18, 767), (19, 769), (130, 1023), (5, 1024), (6, 1025),
                                     (7, 1536), (9, 1537), (7, 2044), (9, 2048), (10, 2049),
-                                    (5, 3072), (6, 3073), (7, 4096), (3, 4097), (4099, 8)])
+                                    (5, 3072), (6, 3073), (7, 4096), (3, 4097), (5, 6144),
+                                    (6, 6145), (7, 8192), (3, 8193), (4099, 8)])
 def test_layernorm_shapes(rows, H):
     say("layernorm rows=%d H=%d" % (rows, H))
     rng = np.random.default_rng(rows * 31 + H)
@@ -175,7 +176,8 @@ def test_layernorm_shapes(rows, H):
 
 @pytest.mark.parametrize("H,x_rs,offset", [(768, 772, 0), (768, 771, 0), (768, 768, 1),
                                           (768, 1000, 3), (1024, 1030, 0), (1024, 1027, 2),
-                                          (2500, 2600, 0), (4096, 4100, 1)])
+                                          (2500, 2600, 0), (4096, 4100, 1), (6000, 6004, 0),
+                                          (8192, 8200, 3)])
 def test_layernorm_strided_and_misaligned(H, x_rs, offset):
     say("layernorm H=%d x_rs=%d offset=%d" % (H, x_rs, offset))
     rng = np.random.default_rng(x_rs + offset)
@@ -185,7 +187,7 @@ def test_layernorm_strided_and_misaligned(H, x_rs, offset):
     check_layernorm(x, g, b, 1e-12, x_rs=x_rs, offset=offset)
 
 
-@pytest.mark.parametrize("H", [96, 1024, 3000])
+@pytest.mark.parametrize("H", [96, 1024, 3000, 7000])
 def test_layernorm_in_place(H):
     say("layernorm in place H=%d" % H)
     rng = np.random.default_rng(5 + H)
@@ -195,7 +197,7 @@ def test_layernorm_in_place(H):
     check_layernorm(x, g, b, 1e-5, in_place=True)
 
 
-@pytest.mark.parametrize("H", [33, 1500])
+@pytest.mark.parametrize("H", [33, 1500, 5000])
 def test_layernorm_extreme_rows(H):
     say("layernorm extreme rows H=%d" % H)
     rows = [np.full(H, 7.5), np.zeros(H), np.full(H, -0.0),
