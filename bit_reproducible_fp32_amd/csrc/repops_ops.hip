@@ -125,272 +125,6 @@ __global__ __launch_bounds__(256) void repops_unary_kernel(const float* x, float
     for (int64_t e = from + t0; e < n; e += stride) y[e] = unary<OP>(x[e]);
 }
 
-// LayerNorm, streaming form (rows longer than the register-resident forms
-// below hold).  The two sums over a row are the fixed-order dimension, so one
-// lane owns a row and walks it in ascending order; rows are the free
-// dimension.  To keep the loads coalesced, a workgroup of kLnThreads lanes owns
-// kLnRows consecutive rows and streams them through LDS in tiles of kLnRows x
-// kLnCols: every lane helps load a tile (consecutive lanes read consecutive
-// floats of a row), then lane r consumes row r of the tile.  Tiles are loaded
-// kLnDepth ahead into registers and double-buffered in LDS.  The output pass
-// has no order to keep, so all lanes stream it directly.
-constexpr int kLnRows = 16;
-constexpr int kLnCols = 64;
-constexpr int kLnThreads = 64;
-constexpr int kLnPitch = kLnCols + 4;            // 16-byte rows, staggered banks
-constexpr int kLnPerThread = kLnRows * kLnCols / kLnThreads;
-constexpr int kLnDepth = 4;                      // tiles in flight per workgroup
-
-struct LnTile {
-    alignas(16) float x[2][kLnRows][kLnPitch];
-    float mu[kLnRows];
-    float rs[kLnRows];
-};
-
-// Loads of one tile (columns c0 .. c0+kLnCols-1 of the block's rows) into
-// registers; out-of-range elements are left as 0 and never consumed.  VEC
-// (x 16-byte aligned, x_rs and H multiples of 4): lane t loads float4 number
-// t + 64k of the tile, so 16 consecutive lanes cover one row's 256 bytes;
-// otherwise element t + 64k.
-struct LnLoad {
-    float v[kLnPerThread];
-};
-
-template <bool VEC>
-__device__ __forceinline__ void ln_load(LnLoad& L, const float* x, int64_t x_rs, int64_t row0,
-                                        int64_t rows, int64_t H, int64_t c0, int tid) {
-    if constexpr (VEC) {
-#pragma unroll
-        for (int k = 0; k < kLnPerThread / 4; ++k) {
-            const int q = tid + k * kLnThreads;
-            const int r = q / (kLnCols / 4), c = 4 * (q % (kLnCols / 4));
-            f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (row0 + r < rows && c0 + c < H)
-                v = *reinterpret_cast<const f32x4*>(x + (row0 + r) * x_rs + c0 + c);
-            L.v[4 * k] = v.x;
-            L.v[4 * k + 1] = v.y;
-            L.v[4 * k + 2] = v.z;
-            L.v[4 * k + 3] = v.w;
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < kLnPerThread; ++k) {
-            const int e = tid + k * kLnThreads;
-            const int r = e / kLnCols, c = e % kLnCols;
-            L.v[k] = (row0 + r < rows && c0 + c < H) ? x[(row0 + r) * x_rs + c0 + c] : 0.0f;
-        }
-    }
-}
-
-// Moves a tile from registers into LDS buffer buf (the inverse of ln_load's
-// mapping).  PASS 0 stores x; PASS 1 stores (x - mu_r)^2, each element as
-// d = x - mu_r and then d * d (every lane computes the same two rounded
-// operations the definition names, so which lane does it does not matter);
-// the owner lanes then only add.
-template <int PASS, bool VEC>
-__device__ __forceinline__ void ln_store(const LnLoad& L, LnTile& T, int buf, int tid) {
-#pragma unroll
-    for (int k = 0; k < kLnPerThread; ++k) {
-        int r, c;
-        if constexpr (VEC) {
-            const int q = tid + (k / 4) * kLnThreads;
-            r = q / (kLnCols / 4);
-            c = 4 * (q % (kLnCols / 4)) + k % 4;
-        } else {
-            const int e = tid + k * kLnThreads;
-            r = e / kLnCols;
-            c = e % kLnCols;
-        }
-        float v = L.v[k];
-        if constexpr (PASS == 1) {
-            const float d = v - T.mu[r];
-            v = d * d;
-        }
-        T.x[buf][r][c] = v;
-    }
-}
-
-// PASS 0: s = s + x; PASS 1: d = x - mu, s = s + d*d; PASS 2: y.
-// One pass over the block's rows.  Tiles are loaded kLnDepth ahead into a
-// ring of registers; tile t+1 moves from the ring into the LDS buffer the
-// consumers are not reading while they consume tile t.
-// PASS 0 returns S = sum of x_i, PASS 1 S2 = sum of (x_i - mu)^2, both from
-// +0 in ascending i (in the owner lane of each row; T.mu holds the means for
-// PASS 1).
-template <int PASS, bool VEC>
-__device__ __forceinline__ float ln_pass(LnTile& T, const float* x, int64_t x_rs, int64_t row0,
-                                         int64_t rows, int64_t H, int tid) {
-    const int64_t ntiles = (H + kLnCols - 1) / kLnCols;
-    const bool owner = tid < kLnRows && row0 + tid < rows;
-    float s = 0.0f;
-    LnLoad ring[kLnDepth];
-#pragma unroll
-    for (int j = 0; j < kLnDepth; ++j)
-        if (j < ntiles) ln_load<VEC>(ring[j], x, x_rs, row0, rows, H, j * kLnCols, tid);
-    ln_store<PASS, VEC>(ring[0], T, 0, tid);
-    __syncthreads();
-    for (int64_t base = 0; base < ntiles; base += kLnDepth) {
-#pragma unroll
-        for (int j = 0; j < kLnDepth; ++j) {
-            const int64_t t = base + j;
-            if (t >= ntiles) break;
-            const int buf = static_cast<int>(t & 1);
-            const int64_t c0 = t * kLnCols;
-            // ring[j] held tile t, already in LDS: refill it with tile t + depth
-            if (t + kLnDepth < ntiles)
-                ln_load<VEC>(ring[j], x, x_rs, row0, rows, H, c0 + kLnDepth * kLnCols, tid);
-            const int64_t left = H - c0;
-            const int cols = left < kLnCols ? static_cast<int>(left) : kLnCols;
-            if (owner) {
-                if (cols == kLnCols) {
-                    // A full tile: all 64 values (and gamma, beta) into
-                    // registers first, then the chain in column order.
-                    f32x4 v[kLnCols / 4];
-#pragma unroll
-                    for (int q = 0; q < kLnCols / 4; ++q)
-                        v[q] = *reinterpret_cast<const f32x4*>(&T.x[buf][tid][4 * q]);
-#pragma unroll
-                    for (int q = 0; q < kLnCols / 4; ++q) {
-                        s = s + v[q].x;
-                        s = s + v[q].y;
-                        s = s + v[q].z;
-                        s = s + v[q].w;
-                    }
-                } else {
-                    for (int c = 0; c < cols; ++c) s = s + T.x[buf][tid][c];
-                }
-            }
-            if (t + 1 < ntiles) ln_store<PASS, VEC>(ring[(j + 1) % kLnDepth], T, buf ^ 1, tid);
-            __syncthreads();
-        }
-    }
-    return s;
-}
-
-// y = ((x - mu) * rstd) * gamma + beta for W consecutive elements (W = 4:
-// 16-byte accesses).
-template <int W>
-struct LnVec {
-    float v[W];
-};
-
-template <int W>
-__device__ __forceinline__ LnVec<W> ln_get(const float* p) {
-    LnVec<W> o;
-    if constexpr (W == 4) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-        o.v[0] = a.x;
-        o.v[1] = a.y;
-        o.v[2] = a.z;
-        o.v[3] = a.w;
-    } else {
-        o.v[0] = p[0];
-    }
-    return o;
-}
-
-template <int W>
-__device__ __forceinline__ void ln_put(float* p, const LnVec<W>& o) {
-    if constexpr (W == 4) {
-        f32x4 a;
-        a.x = o.v[0];
-        a.y = o.v[1];
-        a.z = o.v[2];
-        a.w = o.v[3];
-        *reinterpret_cast<f32x4*>(p) = a;
-    } else {
-        p[0] = o.v[0];
-    }
-}
-
-// Pass 3 has no order to keep: every lane computes outputs, consecutive lanes
-// on consecutive W-element groups of a row, four rows and four groups per
-// lane at a time so that sixteen loads are in flight.  y may be x itself with
-// y_rs == x_rs: each element is read and then written by one lane, after both
-// summing passes, and other workgroups own other rows.
-template <int W>
-__device__ __forceinline__ void ln_output(const LnTile& T, const float* x, int64_t x_rs,
-                                          const float* gamma, const float* beta, float* y,
-                                          int64_t y_rs, int64_t row0, int nr, int64_t H,
-                                          int tid) {
-    constexpr int RU = 4, CU = 4;
-    const int64_t groups = H / W;
-    for (int r0 = 0; r0 < nr; r0 += RU) {
-        for (int64_t gb = 0; gb < groups; gb += CU * kLnThreads) {
-            LnVec<W> v[RU][CU], g[CU], b[CU];
-#pragma unroll
-            for (int u = 0; u < CU; ++u) {
-                const int64_t gi = gb + tid + u * kLnThreads;
-                if (gi < groups) {
-                    if (gamma) g[u] = ln_get<W>(gamma + gi * W);
-                    if (beta) b[u] = ln_get<W>(beta + gi * W);
-#pragma unroll
-                    for (int rr = 0; rr < RU; ++rr)
-                        if (r0 + rr < nr) v[rr][u] = ln_get<W>(x + (row0 + r0 + rr) * x_rs + gi * W);
-                }
-            }
-#pragma unroll
-            for (int rr = 0; rr < RU; ++rr) {
-                if (r0 + rr >= nr) break;
-                const float m = T.mu[r0 + rr], q = T.rs[r0 + rr];
-#pragma unroll
-                for (int u = 0; u < CU; ++u) {
-                    const int64_t gi = gb + tid + u * kLnThreads;
-                    if (gi < groups) {
-                        LnVec<W> o;
-#pragma unroll
-                        for (int w = 0; w < W; ++w) {
-                            const float d = v[rr][u].v[w] - m;
-                            float t = d * q;
-                            if (gamma) t = t * g[u].v[w];
-                            if (beta) t = t + b[u].v[w];
-                            o.v[w] = t;
-                        }
-                        ln_put<W>(y + (row0 + r0 + rr) * y_rs + gi * W, o);
-                    }
-                }
-            }
-        }
-    }
-}
-
-// VEC: x, y, gamma, beta 16-byte aligned; x_rs, y_rs and H multiples of 4.
-template <bool VEC>
-__global__ __launch_bounds__(kLnThreads) void repops_layernorm_kernel(
-    const float* x, int64_t x_rs, const float* __restrict__ gamma,
-    const float* __restrict__ beta, float* y, int64_t y_rs, int64_t rows, int64_t H, float eps,
-    float* __restrict__ mean_out, float* __restrict__ rstd_out) {
-    __shared__ LnTile T;
-    const int tid = static_cast<int>(threadIdx.x);
-    const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kLnRows;
-    const float fh = static_cast<float>(H);
-
-    // pass 1: S = ((+0 + x_0) + x_1) + ...;  mu = S / H (owner lanes)
-    const float s = ln_pass<0, VEC>(T, x, x_rs, row0, rows, H, tid);
-    const float mu = s / fh;
-    if (tid < kLnRows) T.mu[tid] = mu;
-    __syncthreads();
-
-    // pass 2: S2 = sum of (x_i - mu)^2 in the same order; rstd = 1/sqrt(S2/H + eps)
-    const float s2 = ln_pass<1, VEC>(T, x, x_rs, row0, rows, H, tid);
-    const float var = s2 / fh;
-    const float ve = var + eps;
-    const float sd = __builtin_sqrtf(ve);
-    const float rs = 1.0f / sd;
-    if (tid < kLnRows) {
-        T.rs[tid] = rs;
-        if (row0 + tid < rows) {
-            if (mean_out) mean_out[row0 + tid] = mu;
-            if (rstd_out) rstd_out[row0 + tid] = rs;
-        }
-    }
-    __syncthreads();
-
-    // pass 3: y_i = ((x_i - mu) * rstd) * gamma_i + beta_i, all lanes
-    const int nr = rows - row0 < kLnRows ? static_cast<int>(rows - row0) : kLnRows;
-    ln_output<VEC ? 4 : 1>(T, x, x_rs, gamma, beta, y, y_rs, row0, nr, H, tid);
-}
-
 // One step of a ring around each group of L lanes (L = 4 or 16): lane
 // g of a group receives lane (g - 1) mod L's s.  DPP quad permutation
 // [3, 0, 1, 2] for L = 4, row rotation by one for L = 16.
@@ -585,6 +319,152 @@ __global__ __launch_bounds__(64) void repops_layernorm_regs_kernel(
     }
 }
 
+// The ring-streaming form, for rows longer than 2048.  As in the
+// 16-lane register form, a row belongs to 16 consecutive lanes (4 rows per
+// one-wave workgroup) and round j deals elements [64 j, 64 j + 64) out in
+// pieces of 4 (lane g: 64 j + 4 g ...); the fixed-order sums walk the rounds
+// with the same ring step before every piece.  Here the row streams through
+// registers kRsChunk rounds at a time, three times: for the sum, for the sum
+// of squared deviations, and for the output.  Every load is issued
+// unconditionally (positions past H read the row's last piece and are then
+// replaced by +0), and the next chunk is loaded while the current one is
+// summed, so the sums follow the data in.
+constexpr int kRsChunk = 8;  // rounds per chunk
+
+// This lane's pieces of rounds j0 .. j0 + kRsChunk - 1 of the row at xr
+// (hi = H): element k of round j0 + q is a[4 q + k], +0 past H.
+template <bool VEC>
+__device__ __forceinline__ void rs_load(const float* xr, int hi, int j0, int seg,
+                                        float (&a)[4 * kRsChunk]) {
+#pragma unroll
+    for (int q = 0; q < kRsChunk; ++q) {
+        const int o = 64 * (j0 + q) + 4 * seg;
+        if constexpr (VEC) {
+            const bool in = o < hi;
+            const f32x4 t = *reinterpret_cast<const f32x4*>(xr + (in ? o : hi - 4));
+            a[4 * q] = in ? t.x : 0.0f;
+            a[4 * q + 1] = in ? t.y : 0.0f;
+            a[4 * q + 2] = in ? t.z : 0.0f;
+            a[4 * q + 3] = in ? t.w : 0.0f;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const bool in = o + k < hi;
+                const float t = xr[in ? o + k : hi - 1];
+                a[4 * q + k] = in ? t : 0.0f;
+            }
+        }
+    }
+}
+
+// s runs on through one chunk: before each piece a ring step, then the
+// piece's 4 adds.
+__device__ __forceinline__ void rs_sum(float& s, const float (&a)[4 * kRsChunk]) {
+#pragma unroll
+    for (int q = 0; q < kRsChunk; ++q) {
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+            s = ring_step<16>(s);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) s = s + a[4 * q + k];
+        }
+    }
+}
+
+// The same over the squared deviations d = x - mu of one chunk (+0 past H).
+__device__ __forceinline__ void rs_sum_sq(float& s, const float (&a)[4 * kRsChunk], float mu,
+                                          int hi, int j0, int seg) {
+#pragma unroll
+    for (int q = 0; q < kRsChunk; ++q) {
+        float sq[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int e = 64 * (j0 + q) + 4 * seg + k;
+            const float d = e < hi ? a[4 * q + k] - mu : 0.0f;
+            sq[k] = d * d;
+        }
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+            s = ring_step<16>(s);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) s = s + sq[k];
+        }
+    }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(64) void repops_layernorm_stream_kernel(
+    const float* x, int64_t x_rs, const float* __restrict__ gamma,
+    const float* __restrict__ beta, float* y, int64_t y_rs, int64_t rows, int64_t H, float eps,
+    float* __restrict__ mean_out, float* __restrict__ rstd_out) {
+    const int lane = static_cast<int>(threadIdx.x);
+    const int seg = lane & 15;
+    const int hi = static_cast<int>(H);
+    const float fh = static_cast<float>(H);
+    const int rounds = (hi + 63) / 64;
+    const int64_t groups = (rows + 3) / 4;
+    for (int64_t rg = blockIdx.x; rg < groups; rg += gridDim.x) {
+        const int64_t row = rg * 4 + (lane >> 4);
+        const bool live = row < rows;
+        const float* xr = x + (live ? row : 0) * x_rs;
+
+        // S = ((+0 + x_0) + x_1) + ..., a chunk loaded ahead of the one summed
+        float a[4 * kRsChunk], b[4 * kRsChunk];
+        float s = 0.0f;
+        rs_load<VEC>(xr, hi, 0, seg, a);
+        for (int j = 0; j < rounds; j += 2 * kRsChunk) {
+            rs_load<VEC>(xr, hi, j + kRsChunk, seg, b);
+            rs_sum(s, a);
+            rs_load<VEC>(xr, hi, j + 2 * kRsChunk, seg, a);
+            rs_sum(s, b);
+        }
+        s = __shfl(s, 15, 16);
+        const float mu = s / fh;
+
+        // S2 = sum of (x_i - mu) * (x_i - mu), the same way
+        float s2 = 0.0f;
+        rs_load<VEC>(xr, hi, 0, seg, a);
+        for (int j = 0; j < rounds; j += 2 * kRsChunk) {
+            rs_load<VEC>(xr, hi, j + kRsChunk, seg, b);
+            rs_sum_sq(s2, a, mu, hi, j, seg);
+            rs_load<VEC>(xr, hi, j + 2 * kRsChunk, seg, a);
+            rs_sum_sq(s2, b, mu, hi, j + kRsChunk, seg);
+        }
+        s2 = __shfl(s2, 15, 16);
+        const float var = s2 / fh;
+        const float ve = var + eps;
+        const float sd = __builtin_sqrtf(ve);
+        const float rs = 1.0f / sd;
+        if (live && seg == 0) {
+            if (mean_out) mean_out[row] = mu;
+            if (rstd_out) rstd_out[row] = rs;
+        }
+
+        // y_i = ((x_i - mu) * rstd) * gamma_i + beta_i; a missing gamma acts
+        // as 1 and a missing beta as -0 (t * 1 == t, t + (-0) == t)
+        float* yr = y + (live ? row : 0) * y_rs;
+        const bool has_g = gamma != nullptr, has_b = beta != nullptr;
+        for (int j = 0; j < rounds; j += kRsChunk) {
+            float gv[4 * kRsChunk], bv[4 * kRsChunk];
+            rs_load<VEC>(xr, hi, j, seg, a);
+            rs_load<VEC>(has_g ? gamma : xr, hi, j, seg, gv);
+            rs_load<VEC>(has_b ? beta : xr, hi, j, seg, bv);
+#pragma unroll
+            for (int q = 0; q < kRsChunk; ++q) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int e = 64 * (j + q) + 4 * seg + k;
+                    float t = a[4 * q + k] - mu;
+                    t = t * rs;
+                    t = t * (has_g ? gv[4 * q + k] : 1.0f);
+                    t = t + (has_b ? bv[4 * q + k] : -0.0f);
+                    if (live && e < hi) yr[e] = t;
+                }
+            }
+        }
+    }
+}
+
 }  // namespace
 
 int launch_unary(int op, const float* x, float* y, int64_t n, bool vec, void* stream) {
@@ -606,11 +486,13 @@ int launch_layernorm(const float* x, int64_t x_rs, const float* gamma, const flo
                      int64_t y_rs, int64_t rows, int64_t H, float eps, float* mean, float* rstd,
                      bool vec, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    // Register-resident forms for rows of at most 4096 elements: a quad of
+    // Register-resident forms for rows of at most 2048 elements: a quad of
     // lanes per row up to 768 (16 rows per wave), 16 lanes per row above
     // (4 rows per wave).  S (elements per lane) is the smallest that holds
-    // the row, since every sum walks all L * S slots.
-    if (H <= 4096) {
+    // the row, since every sum walks all L * S slots.  (Forms for 3072 and
+    // 4096 would need 269 and 462 VGPRs, one wave per SIMD; the streaming
+    // form below matches them there and is faster in between.)
+    if (H <= 2048) {
         using Gn = void (*)(const float*, int64_t, const float*, const float*, float*, int64_t,
                             int64_t, int64_t, float, float*, float*);
         Gn gn;
@@ -633,15 +515,9 @@ int launch_layernorm(const float* x, int64_t x_rs, const float* gamma, const flo
         } else if (H <= 1536) {
             gn = vec ? repops_layernorm_regs_kernel<16, 96, true>
                      : repops_layernorm_regs_kernel<16, 96, false>;
-        } else if (H <= 2048) {
+        } else {
             gn = vec ? repops_layernorm_regs_kernel<16, 128, true>
                      : repops_layernorm_regs_kernel<16, 128, false>;
-        } else if (H <= 3072) {
-            gn = vec ? repops_layernorm_regs_kernel<16, 192, true>
-                     : repops_layernorm_regs_kernel<16, 192, false>;
-        } else {
-            gn = vec ? repops_layernorm_regs_kernel<16, 256, true>
-                     : repops_layernorm_regs_kernel<16, 256, false>;
         }
         const int64_t groups = (rows + rows_per_wave - 1) / rows_per_wave;
         const int64_t gblocks = groups < (int64_t(1) << 20) ? groups : (int64_t(1) << 20);
@@ -649,13 +525,14 @@ int launch_layernorm(const float* x, int64_t x_rs, const float* gamma, const flo
                            gamma, beta, y, y_rs, rows, H, eps, mean, rstd);
         return static_cast<int>(hipGetLastError());
     }
-    // Longer rows stream through LDS.
-    const int64_t blocks = (rows + kLnRows - 1) / kLnRows;
+    // Longer rows stream through registers, 16 lanes per row.
+    const int64_t groups = (rows + 3) / 4;
+    const int64_t blocks = groups < (int64_t(1) << 20) ? groups : (int64_t(1) << 20);
     using Fn = void (*)(const float*, int64_t, const float*, const float*, float*, int64_t,
                         int64_t, int64_t, float, float*, float*);
-    Fn fn = vec ? repops_layernorm_kernel<true> : repops_layernorm_kernel<false>;
-    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(kLnThreads), 0, s, x, x_rs,
-                       gamma, beta, y, y_rs, rows, H, eps, mean, rstd);
+    Fn fn = vec ? repops_layernorm_stream_kernel<true> : repops_layernorm_stream_kernel<false>;
+    hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(64), 0, s, x, x_rs, gamma,
+                       beta, y, y_rs, rows, H, eps, mean, rstd);
     return static_cast<int>(hipGetLastError());
 }
 
