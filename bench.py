@@ -308,6 +308,8 @@ def main():
         "cpu_baseline": cpu,
         "bitexact_sampled": bitexact,
         "sha256_C": h,
+        "sha256_inputs": {"A": hashlib.sha256(A.tobytes()).hexdigest(),
+                          "B": hashlib.sha256(B.tobytes()).hexdigest()},
         "kernel_ms": {"mean": round(k_avg_ms, 4)},
     }
     rec.update(extra)
