@@ -215,6 +215,27 @@ def test_layernorm_extreme_rows(H):
             check_layernorm(x, None, None, eps)
 
 
+def test_layernorm_random_configurations():
+    """40 seeded random configurations across every kernel form: H log-uniform
+    in [1, 20000], 1 to 300 rows, padded row strides, misaligned starts,
+    gamma and beta present or not, four eps values."""
+    rng = np.random.default_rng(2024)
+    for case in range(40):
+        H = int(np.exp(rng.uniform(0, np.log(20000))))
+        rows = int(rng.integers(1, 301))
+        rows = max(1, min(rows, 1_500_000 // max(H, 1)))
+        pad = int(rng.integers(0, 8)) if rng.random() < 0.5 else 0
+        offset = int(rng.integers(0, 4)) if rng.random() < 0.5 else 0
+        eps = float(rng.choice([0.0, 1e-12, 1e-5, 0.5]))
+        x = (rng.standard_normal((rows, H)) * rng.uniform(0.01, 100) + rng.uniform(-10, 10)
+             ).astype(np.float32)
+        g = rng.standard_normal(H).astype(np.float32) if rng.random() < 0.7 else None
+        b = rng.standard_normal(H).astype(np.float32) if rng.random() < 0.7 else None
+        say("layernorm random case %d: rows=%d H=%d pad=%d offset=%d gamma=%s beta=%s eps=%g"
+            % (case, rows, H, pad, offset, g is not None, b is not None, eps))
+        check_layernorm(x, g, b, eps, x_rs=H + pad, offset=offset)
+
+
 def test_layernorm_torch_wrapper():
     say("layernorm torch wrapper")
     rng = np.random.default_rng(6)
