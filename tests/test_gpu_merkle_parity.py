@@ -3,9 +3,10 @@ re-execution of a disputed matmul (repops_referee_matmul_f32), through the C
 ABI, against the CPU oracle (oracle/merkle.py), byte for byte.
 
 Covered: the empty input; one-block and two-block padding boundaries; a
-tree of exactly one workgroup (256 leaves) and trees needing two and three
-launches (the first folds groups of 256 leaves, later ones groups of 1024
-digests); leaf sizes from 4 bytes to 2^24 bytes; the narrow-load path
+tree of exactly one workgroup (256 leaves) and trees needing two, three and
+four launches (the first hashes the leaves and folds 0, 2 or more levels
+depending on the leaf size, later ones fold groups of 1024 digests); leaf
+sizes from 4 bytes to 2^24 bytes, and seeded random sizes and leaf lengths; the narrow-load path
 (leaves not a multiple of 16 bytes, data only 4-byte aligned); workspace
 reuse across calls; the tensor hash of matmul outputs; the referee's verdicts
 (an honest claim, a claim one bit off, a claim from another summation order,
@@ -64,10 +65,13 @@ CASES = [
     (116, 1024, 0), (120, 1024, 0), (124, 1024, 0), (128, 1024, 0),
     (1024, 1024, 0), (1028, 1024, 0),
     (256 * 1024, 1024, 0),          # 256 leaves: one launch
-    (256 * 1024 + 4, 1024, 0),      # 257 leaves: two launches
-    (65536 * 4, 4, 0),              # 65536 leaves: two launches
-    (65537 * 4, 4, 0),              # 257 digests after the first launch
-    ((256 * 1024 + 1) * 4, 4, 0),   # 262145 leaves: three launches
+    (256 * 1024 + 4, 1024, 0),      # 257 leaves: 257 digests, then the root
+    (1025 * 1024, 1024, 0),         # 1025 digests: three launches
+    (65536 * 4, 4, 0),              # 4-byte leaves fold 6 levels: 1024 digests
+    (65537 * 4, 4, 0),              # 1025 digests: three launches
+    ((1024 * 1024 + 1) * 1024, 1024, 0),  # 1048577 digests: four launches (1 GiB)
+    (4097 * 256, 256, 0),           # 256-byte leaves fold 2 levels: 1025 digests
+    (4096 * 1020 + 8, 1020, 0),     # just under 1 KiB: 2 levels, last leaf short
     (1000 * 52 + 12, 52, 0),        # leaves not a multiple of 16 bytes
     (300 * 1024 + 8, 1024, 1),      # data 4-byte but not 16-byte aligned
     (77 * 4096 + 2048, 4096, 0),
@@ -82,6 +86,21 @@ def test_root_of_bytes(nbytes, leaf, offset):
     data = random_bytes(nbytes, seed=nbytes * 7 + leaf)
     got = rp.merkle_root(on_gpu(data, offset), leaf_bytes=leaf)
     assert got == merkle.merkle_root(data.tobytes(), leaf)
+
+
+def test_random_sizes_and_leaf_lengths():
+    """12 seeded random (size, leaf length, alignment) cases on both sides of
+    the first launch's fold policy."""
+    rng = np.random.default_rng(77)
+    for case in range(12):
+        leaf = 4 * int(rng.integers(1, 1025))               # 4 .. 4096 bytes
+        n_leaves = int(rng.integers(1, 20001))
+        nbytes = max(0, (n_leaves - 1) * leaf + 4 * int(rng.integers(1, leaf // 4 + 1)))
+        offset = int(rng.integers(0, 4))
+        say("random case %d: nbytes=%d leaf=%d offset=%d" % (case, nbytes, leaf, offset))
+        data = random_bytes(nbytes, seed=1000 + case)
+        got = rp.merkle_root(on_gpu(data, offset), leaf_bytes=leaf)
+        assert got == merkle.merkle_root(data.tobytes(), leaf), case
 
 
 def test_workspace_reused_across_calls_and_async_out():
