@@ -47,6 +47,8 @@ __device__ __forceinline__ void fold_at(const FoldArgs& G, int n, bool first, bo
                                         float* sum, float* theta, float* gbar, float inv_k,
                                         float eta, int64_t e) {
     V s = first ? ld<V>(G.g[0] + e) : ld<V>(sum + e);
+    V th;
+    if (last) th = ld<V>(theta + e);  // issued with the gradients' loads
     for (int c = first ? 1 : 0; c < n; c += 8) {
         V x[8];
 #pragma unroll
@@ -63,7 +65,7 @@ __device__ __forceinline__ void fold_at(const FoldArgs& G, int n, bool first, bo
     const V gb = inv_k * s;
     if (gbar) st<V>(gbar + e, gb);
     const V step = eta * gb;
-    st<V>(theta + e, ld<V>(theta + e) - step);
+    st<V>(theta + e, th - step);
 }
 
 // VEC: every pointer is 16-byte aligned; float4 over the first 4*(d/4)
