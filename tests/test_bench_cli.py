@@ -7,12 +7,19 @@ import os
 import subprocess
 import sys
 
+import pytest
+
 from bit_reproducible_fp32_amd import inputs
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def run(*args):
+    # A child process is started only from a process that has not touched the
+    # GPU (its state must not be carried into another program).
+    torch = sys.modules.get("torch")
+    if torch is not None and torch.cuda.is_initialized():
+        pytest.skip("the GPU is initialised in this process")
     return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
                           capture_output=True, text=True, timeout=120, cwd=ROOT)
 
@@ -38,3 +45,4 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""        # no JSON line
+
