@@ -668,15 +668,34 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void repops_mprod_kernel(
     }
 
     // Epilogue: for each register v, lanes 0-31 and 32-63 each write 32
-    // consecutive columns of one row.
+    // consecutive columns of one row, row i0 + r(v) with r(v) = mprod_row(v, 0)
+    // (i0 holds the lane's 4-row shift).  With a bias, the sums become
+    // RN(sum + bias[j]) in place first, so the one load is waited for before
+    // any store (on gfx9 one counter tracks loads and stores: a wait placed
+    // between stores would also wait for every store issued before it).  A
+    // tile wholly inside M stores without row tests.
+    const int64_t i0 = m0 + wm * 64 + 4 * (lane >> 5);
+    const int64_t rows_left = M - i0;  // rows i0 + r exist for r < rows_left
+    const bool full_m = m0 + BM <= M;
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
         const int64_t j = n0 + wn * 32 * TN + t * 32 + (lane & 31);
         if (j >= N) continue;
+        if (C.bias) {
+            const float b = C.bias[j * C.bias_s];
 #pragma unroll
-        for (int v = 0; v < 32; ++v) {
-            const int64_t i = m0 + wm * 64 + mprod_row(v, lane);
-            if (i < M) C.p[i * C.s_i + j * C.s_j] = epilogue_value(C, j, acc[t][v]);
+            for (int v = 0; v < 32; ++v) acc[t][v] = add_rn(acc[t][v], b);
+        }
+        float* const cp = C.p + i0 * C.s_i + j * C.s_j;
+        if (full_m) {
+#pragma unroll
+            for (int v = 0; v < 32; ++v) cp[mprod_row(v, 0) * C.s_i] = acc[t][v];
+        } else {
+#pragma unroll
+            for (int v = 0; v < 32; ++v) {
+                const int r = mprod_row(v, 0);
+                if (r < rows_left) cp[r * C.s_i] = acc[t][v];
+            }
         }
     }
 }
