@@ -231,6 +231,32 @@ def test_isa_matrix_product_kernels_only_form_single_products():
         assert "v_add_f32" in body and "v_mul_f32" not in body, name
 
 
+def _longest_store_run_without_wait(body):
+    best = cur = 0
+    for line in body.splitlines():
+        t = line.strip()
+        if t.startswith("global_store"):
+            cur += 1
+            best = max(best, cur)
+        elif t.startswith("s_waitcnt") and "vmcnt" in t:
+            cur = 0
+    return best
+
+
+def test_isa_matrix_product_epilogue_stores_do_not_wait():
+    """The 32-wide matrix-core product kernel stores a lane's 32 sums of a
+    column block with no memory-counter wait between the stores. On gfx9 one
+    counter tracks loads and stores, so a wait placed between two stores
+    (for example for a bias load) would make each store wait for the one
+    before it. In every instantiation, at least 32 consecutive stores have no
+    vmcnt wait between them."""
+    bodies, _ = kernels()
+    mprod = {n: b for n, b in bodies.items() if "mprod_kernel" in n and "mprod16" not in n}
+    assert len(mprod) >= 9
+    for name, body in mprod.items():
+        assert _longest_store_run_without_wait(body) >= 32, name
+
+
 def test_isa_mul_and_add_present_in_tiled_kernels():
     bodies, _ = kernels()
     tiled = [b for n, b in bodies.items() if "tiled_kernel" in n]
