@@ -54,8 +54,11 @@ def run(a, b, **kw):
     return c.cpu().numpy()
 
 
-def test_every_variant_with_and_without_bias():
-    Bn, M, N, K = 3, 70, 90, 37
+@pytest.mark.parametrize("M", [70, 300])
+def test_every_variant_with_and_without_bias(M):
+    """M = 70: only edge tiles for 128- and 256-row tiles; M = 300: whole
+    tiles inside M and a ragged last tile, for every tile shape."""
+    Bn, N, K = 3, 90, 37
     A = inputs.random_matrix((Bn * M, K), 401).reshape(Bn, M, K)
     B = inputs.random_matrix((Bn * K, N), 402, "normal0.02").reshape(Bn, K, N)
     bias = inputs.random_matrix((Bn, N), 403)
