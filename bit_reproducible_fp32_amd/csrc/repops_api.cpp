@@ -20,7 +20,7 @@ using namespace repops;
 
 namespace {
 
-enum Kind { KIND_NAIVE = 0, KIND_TILED = 1, KIND_MPROD = 2 };
+enum Kind { KIND_NAIVE = 0, KIND_TILED = 1, KIND_MPROD = 2, KIND_SROW = 3 };
 
 struct Variant {
     const char* name;
@@ -51,6 +51,13 @@ const Variant kVariants[] = {
     {"mprod16_t128x128x32_w16_xcd", KIND_MPROD, M16CFG_128x128_W16, ORDER_XCD_GROUP},
     {"mprod16_t128x64x32_w8_xcd", KIND_MPROD, M16CFG_128x64_W8, ORDER_XCD_GROUP},
     {"mprod16_t128x128x16_w8_xcd", KIND_MPROD, M16CFG_128x128_W8, ORDER_XCD_GROUP},
+    {"srow_t4x64x32_r1c1_w4_row", KIND_SROW, SCFG_R1C1_W4, ORDER_ROW},
+    {"srow_t16x64x32_r4c1_w4_row", KIND_SROW, SCFG_R4C1_W4, ORDER_ROW},
+    {"srow_t16x64x32_r4c1_w4_xcd", KIND_SROW, SCFG_R4C1_W4, ORDER_XCD_GROUP},
+    {"srow_t8x128x32_r2c2_w4_row", KIND_SROW, SCFG_R2C2_W4, ORDER_ROW},
+    {"srow_t32x64x32_r8c1_w4_col", KIND_SROW, SCFG_R8C1_W4, ORDER_COL},
+    {"srow_t32x128x32_r4c2_w8_xcd", KIND_SROW, SCFG_R4C2_W8, ORDER_XCD_GROUP},
+    {"srow_t64x128x32_r8c2_w8_xcd", KIND_SROW, SCFG_R8C2_W8, ORDER_XCD_GROUP},
 };
 constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -197,17 +204,38 @@ int classify(const OperandView& v, int64_t K, int64_t batch) {
 
 int pick(const Problem& p) {
     static const int large = variant_index("mprod1_t128x128x16_w8_xcd");
-    static const int small = variant_index("valu_t64x64x16_r4x4_row");
+    static const int medium = variant_index("srow_t32x128x32_r4c2_w8_xcd");
+    static const int small = variant_index("srow_t16x64x32_r4c1_w4_xcd");
+    static const int tiny = variant_index("srow_t4x64x32_r1c1_w4_row");
     const int64_t tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch;
-    // 256 CUs: 128x128 product tiles when there are at least two per CU;
-    // below that the problem cannot fill the chip and the 64x64 VALU tiles
-    // (more workgroups, measured faster at 256^3 and 1024^3) win.
-    return tiles >= 512 ? large : small;
+    const int64_t outputs = p.M * p.N * p.batch;
+    // 256 CUs.  128x128 product tiles from one per CU up (measured fastest
+    // from 2048 x 2048 outputs).  Below that the scalar-row kernels, with few
+    // outputs per lane, still give every SIMD several waves: 8 outputs per
+    // lane from 2^19 outputs (fastest at 1024 x 1024), 4 from 2^17, and one
+    // below (fastest at 256 x 256).
+    if (tiles >= 256) return large;
+    if (outputs >= (int64_t(1) << 19)) return medium;
+    if (outputs >= (int64_t(1) << 17)) return small;
+    return tiny;
+}
+
+// The scalar-row kernels count k, and A's byte offsets along k, in 32 bits;
+// beyond that the register-blocked VALU kernel runs instead (every variant
+// gives the same bits).
+constexpr int64_t kSrowMaxK = (int64_t(1) << 30) - 1;
+
+int runnable(int v, const Problem& p) {
+    if (kVariants[v].kind == KIND_SROW && p.K > kSrowMaxK) {
+        static const int fallback = variant_index("valu_t64x64x16_r4x4_row");
+        return fallback;
+    }
+    return v;
 }
 
 repops_status run(const Problem& p, int variant, void* stream) {
     if (p.M == 0 || p.N == 0 || p.batch == 0) return REPOPS_OK;
-    const int v = p.K == 0 ? -1 : (variant < 0 ? pick(p) : variant);
+    const int v = p.K == 0 ? -1 : runnable(variant < 0 ? pick(p) : variant, p);
     const int la = p.K == 0 ? 0 : classify(p.a, p.K, p.batch);
     const int lb = p.K == 0 ? 0 : classify(p.b, p.K, p.batch);
     // The grid's batch dimension is limited; longer batches run in chunks.
@@ -224,6 +252,9 @@ repops_status run(const Problem& p, int variant, void* stream) {
             err = launch_fill_zero(c, p.M, p.N, nb, stream);
         } else if (kVariants[v].kind == KIND_NAIVE) {
             err = launch_naive(a, b, c, p.M, p.N, p.K, nb, stream);
+        } else if (kVariants[v].kind == KIND_SROW) {
+            err = launch_srow(kVariants[v].cfg, la, lb, a, b, c, p.M, p.N, p.K, nb,
+                              kVariants[v].order, stream);
         } else if (kVariants[v].kind == KIND_MPROD) {
             err = launch_mprod(kVariants[v].cfg, la, lb, a, b, c, p.M, p.N, p.K, nb,
                                kVariants[v].order, stream);
@@ -290,7 +321,7 @@ int repops_pick_variant_f32(const float* A, int64_t a_rs, int64_t a_cs, const fl
     if (check_operands(A, 0, a_rs, a_cs, B, 0, b_rs, b_cs, M, N, K, 1, trans_a, trans_b, &p, &ae,
                        &be) != REPOPS_OK)
         return -1;
-    return pick(p);
+    return runnable(pick(p), p);
 }
 
 int repops_variant_count(void) { return kNumVariants; }

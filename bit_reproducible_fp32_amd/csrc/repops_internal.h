@@ -58,6 +58,15 @@ enum TileCfg : int {
     M16CFG_128x128_W16 = 11,  // 2x8 waves, TN=1 (1024 lanes), BK=32
     M16CFG_128x64_W8 = 12,    // 2x4 waves, TN=1, BK=32
     M16CFG_128x128_W8 = 13,   // 2x4 waves, TN=2
+    // Scalar-row kernels (each wave's A values wave-uniform in SGPRs, products
+    // and sums on the VALU): rows per wave R, 64-column groups per lane C,
+    // waves W; 32-deep k-tiles.
+    SCFG_R1C1_W4 = 14,  // 4 x 64 tile
+    SCFG_R4C1_W4 = 15,  // 16 x 64
+    SCFG_R2C2_W4 = 16,  // 8 x 128
+    SCFG_R8C1_W4 = 17,  // 32 x 64
+    SCFG_R4C2_W8 = 18,  // 32 x 128
+    SCFG_R8C2_W8 = 19,  // 64 x 128
 };
 
 // Workgroup -> output-tile traversal orders (never change a bit).
@@ -92,6 +101,8 @@ int launch_tiled(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, Ou
                  int64_t M, int64_t N, int64_t K, int64_t batch, int order, void* stream);
 int launch_mprod(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, OutView C,
                  int64_t M, int64_t N, int64_t K, int64_t batch, int order, void* stream);
+int launch_srow(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, OutView C,
+                int64_t M, int64_t N, int64_t K, int64_t batch, int order, void* stream);
 int launch_naive(OperandView A, OperandView B, OutView C, int64_t M, int64_t N, int64_t K,
                  int64_t batch, void* stream);
 int launch_fill_zero(OutView C, int64_t M, int64_t N, int64_t batch, void* stream);

@@ -17,6 +17,8 @@
 // addends are -0).  So padding does not change a bit.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "repops_internal.h"
 
 #pragma clang fp contract(off)
@@ -352,6 +354,247 @@ __global__ __launch_bounds__(kThreads) void repops_tiled_kernel(OperandView A, O
                 }
             }
         }
+}
+
+// ---------------------------------------------------------------------------
+// Scalar-row kernel.  Each wave owns R whole rows of a BM x BN output tile
+// (BM = R * W for W waves, BN = 64 * CN), so for every k the R values
+// op(A)(i, k) the wave needs are the same in all 64 lanes.  They come in
+// through scalar loads into SGPRs, AK consecutive k at a time, one chunk
+// ahead of use, and every v_mul_f32 takes one of them as its scalar operand.
+// Lane l owns the CN columns n0 + l + 64c; its B values come from the
+// k-major LDS tile (double-buffered, staged as in the other kernels), read
+// one chunk ahead.  A lane reads 1/R LDS words per multiply-accumulate and
+// needs only R x CN outputs: a problem too small to fill the chip with the
+// register-blocked tiles still gets several waves per SIMD.
+//
+// Rows beyond M are clamped to row M-1 (their sums are never stored); k >= K
+// reads +0 for A (a clamped, in-bounds address, then a uniform select) and for
+// B (the tile loader), so a padded step adds +0 to s and changes no bit.
+//
+// A is read through the constant address space: it is not written while the
+// kernel runs (the host refuses a C that overlaps it), and a wave-uniform load
+// from that space is always a scalar load.
+typedef const __attribute__((address_space(4))) float* ConstF32Ptr;
+
+// A wave-uniform pointer held in SGPRs (64-bit compares and multiplies may be
+// formed on the VALU, so a value derived from them is moved back explicitly).
+__device__ __forceinline__ ConstF32Ptr uniform_ptr(ConstF32Ptr p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
+    const uint32_t hi =
+        static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v >> 32)));
+    return reinterpret_cast<ConstF32Ptr>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+template <int R, int CN, int W, int BK, int LA, int LB>
+__global__ __launch_bounds__(64 * W) void repops_srow_kernel(OperandView A, OperandView B,
+                                                             OutView C, int64_t M, int64_t N,
+                                                             int64_t K, TileGrid grid) {
+    constexpr int NT = 64 * W;
+    constexpr int BM = R * W, BN = 64 * CN;
+    constexpr int LDB = BN + kPad;
+    // k values per row in one scalar chunk: two chunks (the one in use and the
+    // next) of R x AK SGPRs stay within 32 registers, next to the kernel
+    // arguments and addresses that also live in SGPRs.
+    constexpr int AK = (R >= 8) ? 2 : (R >= 4 ? 4 : (R >= 2 ? 8 : 16));
+    constexpr int CHUNKS = BK / AK;  // chunks per k-tile
+    static_assert(BK % AK == 0, "a k-tile holds whole scalar chunks");
+
+    __shared__ __attribute__((aligned(16))) float Bs[2][BK * LDB];
+
+    const int tid = static_cast<int>(threadIdx.x);
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int tm, tn;
+    tile_of_block(grid, tm, tn);
+    select_batch(A, B, C);
+    const int64_t m0 = static_cast<int64_t>(tm) * BM;
+    const int64_t n0 = static_cast<int64_t>(tn) * BN;
+
+    // This wave's rows of op(A), clamped into the operand.
+    const ConstF32Ptr a0 = (ConstF32Ptr)(A.p);
+    const int64_t sk = (LA == LAY_KC) ? 1 : A.s_k;
+    const int64_t sx = (LA == LAY_XC) ? 1 : A.s_x;
+    ConstF32Ptr pa[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t i = m0 + wave * R + r;
+        pa[r] = uniform_ptr(a0 + (i < M ? i : M - 1) * sx);
+    }
+    // Loads the next scalar chunk.  Rows stored along k (LAY_KC) keep fixed
+    // row pointers and one 32-bit byte offset, which the scalar load takes as
+    // its offset register (one scalar add per chunk; the host launches these
+    // kernels only for K < 2^30).  Other layouts walk each row pointer along
+    // k.  The offset or pointers pass through an empty asm first, so the
+    // compiler cannot hoist or merge the loads of later chunks: only two
+    // chunks are ever live in SGPRs.
+    uint32_t koff = 0;
+    auto load_chunk = [&](float (&dst)[R][AK]) {
+        if constexpr (LA == LAY_KC) {
+            asm volatile("" : "+s"(koff));
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const ConstF32Ptr p =
+                    (ConstF32Ptr)((const __attribute__((address_space(4))) char*)(pa[r]) + koff);
+#pragma unroll
+                for (int kk = 0; kk < AK; ++kk) dst[r][kk] = p[kk];
+            }
+            koff += AK * 4;
+        } else {
+#pragma unroll
+            for (int r = 0; r < R; ++r) asm volatile("" : "+s"(pa[r]));
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int kk = 0; kk < AK; ++kk) dst[r][kk] = pa[r][kk * sk];
+#pragma unroll
+            for (int r = 0; r < R; ++r) pa[r] = uniform_ptr(pa[r] + AK * sk);
+        }
+    };
+
+    float acc[R][CN];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < CN; ++c) acc[r][c] = 0.0f;  // s = +0
+
+    // k bookkeeping is 32-bit, so each test on it is a scalar compare and the
+    // values it selects stay in SGPRs.
+    TileStage<BN, BK, LB, NT> sb;
+    sb.init(B, n0, tid);
+    const int Kr = static_cast<int>(K);
+    const int nfull = Kr / BK;                 // k-tiles entirely inside [0, K)
+    const bool tail = (Kr % BK) != 0;
+
+    float ac[R][AK];
+    if (nfull > 0) {
+        load_chunk(ac);
+        sb.load_full();
+    } else {
+        sb.load_tail(0, K, B.s_k);
+    }
+    sb.store(Bs[0], tid);
+    __syncthreads();
+
+    auto read_b = [&](float (&dst)[AK][CN], const float* bk) {
+#pragma unroll
+        for (int kk = 0; kk < AK; ++kk)
+#pragma unroll
+            for (int c = 0; c < CN; ++c) dst[kk][c] = bk[kk * LDB + 64 * c];
+    };
+    // One whole k-tile.  Every scalar chunk of it lies inside [0, K); the
+    // next chunk's scalar loads go out before the current chunk's steps,
+    // except after the last chunk of the last whole tile (LAST), where there
+    // is no next whole chunk.  B values are read one chunk ahead inside the
+    // tile.
+    auto whole_tile = [&](int kt, auto last) {
+        constexpr bool LAST = decltype(last)::value;
+        const bool more = !LAST || tail;
+        if (!LAST) sb.load_full();
+        else if (tail) sb.load_tail(static_cast<int64_t>(nfull) * BK, K, B.s_k);
+        asm volatile("" ::: "memory");
+        const float* bs = &Bs[kt & 1][lane];
+        float bc[AK][CN];
+        read_b(bc, bs);
+#pragma unroll
+        for (int h = 0; h < CHUNKS; ++h) {
+            // Scalar loads and LDS reads share one completion counter and
+            // scalar loads may return out of order, so everything issued
+            // before is waited for here (the empty asm uses this chunk's B
+            // values): this chunk's B values and A chunk, both issued one
+            // chunk earlier.  Then the next chunk's LDS reads and scalar loads
+            // go out, and overlap this chunk's arithmetic.
+#pragma unroll
+            for (int kk = 0; kk < AK; ++kk)
+#pragma unroll
+                for (int c = 0; c < CN; ++c) asm volatile("" ::"v"(bc[kk][c]));
+            float bn[AK][CN];
+            if (h + 1 < CHUNKS) read_b(bn, bs + (h + 1) * AK * LDB);
+            // (a constant once the loop over h is unrolled)
+            const bool next = !LAST || h + 1 < CHUNKS;
+            float an[R][AK];
+            if (next) load_chunk(an);
+            // Nothing moves across: the loads stay ahead of the arithmetic.
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kk = 0; kk < AK; ++kk)
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int c = 0; c < CN; ++c)
+                        acc[r][c] = add_rn(acc[r][c], mul_rn(ac[r][kk], bc[kk][c]));
+            // Pin this chunk's adds here, ahead of the next chunk's waits.
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int c = 0; c < CN; ++c) asm volatile("" : "+v"(acc[r][c]));
+            if (next) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int kk = 0; kk < AK; ++kk) ac[r][kk] = an[r][kk];
+            }
+            if (h + 1 < CHUNKS) {
+#pragma unroll
+                for (int kk = 0; kk < AK; ++kk)
+#pragma unroll
+                    for (int c = 0; c < CN; ++c) bc[kk][c] = bn[kk][c];
+            }
+        }
+        asm volatile("" ::: "memory");
+        if (more) sb.store(Bs[(kt + 1) & 1], tid);
+        __syncthreads();
+    };
+    for (int kt = 0; kt + 1 < nfull; ++kt) whole_tile(kt, std::false_type{});
+    if (nfull > 0) whole_tile(nfull - 1, std::true_type{});
+
+    // The partial last k-tile: k >= K reads +0 on both sides (for A, a
+    // clamped in-bounds load, then a uniform select kept scalar).
+    if (tail) {
+        const float* bs = &Bs[nfull & 1][lane];
+        const int rem = Kr - nfull * BK;
+        ConstF32Ptr pt[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t i = m0 + wave * R + r;
+            pt[r] = uniform_ptr(a0 + (i < M ? i : M - 1) * sx +
+                                static_cast<int64_t>(nfull) * BK * sk);
+        }
+#pragma unroll 1
+        for (int kk = 0; kk < BK; ++kk) {
+            float b[CN];
+#pragma unroll
+            for (int c = 0; c < CN; ++c) b[c] = bs[kk * LDB + 64 * c];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float v = pt[r][(kk < rem ? kk : rem - 1) * sk];
+                const float a = __int_as_float(
+                    __builtin_amdgcn_readfirstlane(__float_as_int(kk < rem ? v : 0.0f)));
+#pragma unroll
+                for (int c = 0; c < CN; ++c) acc[r][c] = add_rn(acc[r][c], mul_rn(a, b[c]));
+            }
+        }
+    }
+
+    // Epilogue: each row's CN sums, 64 consecutive columns per store.
+    float bias[CN];
+#pragma unroll
+    for (int c = 0; c < CN; ++c) {
+        const int64_t j = n0 + lane + 64 * c;
+        bias[c] = (C.bias != nullptr && j < N) ? C.bias[j * C.bias_s] : 0.0f;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int64_t i = m0 + wave * R + r;
+        if (i >= M) continue;
+#pragma unroll
+        for (int c = 0; c < CN; ++c) {
+            const int64_t j = n0 + lane + 64 * c;
+            if (j < N)
+                C.p[i * C.s_i + j * C.s_j] = C.bias ? add_rn(acc[r][c], bias[c]) : acc[r][c];
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -776,6 +1019,20 @@ struct Mprod16Table {
     }
 };
 
+template <int R, int CN, int W, int BK>
+struct SrowTable {
+    template <int LA, int LB>
+    static constexpr TiledFn fn() { return &repops_srow_kernel<R, CN, W, BK, LA, LB>; }
+    static TiledFn get(int la, int lb) {
+        static const TiledFn t[LAY_COUNT][LAY_COUNT] = {
+            {fn<0, 0>(), fn<0, 1>(), fn<0, 2>()},
+            {fn<1, 0>(), fn<1, 1>(), fn<1, 2>()},
+            {fn<2, 0>(), fn<2, 1>(), fn<2, 2>()},
+        };
+        return t[la][lb];
+    }
+};
+
 }  // namespace
 
 FastDiv make_fastdiv(uint32_t d) {
@@ -816,6 +1073,12 @@ void tile_shape(int cfg, int* bm, int* bn) {
         case M16CFG_128x128_W16: *bm = 128; *bn = 128; break;
         case M16CFG_128x64_W8: *bm = 128; *bn = 64; break;
         case M16CFG_128x128_W8: *bm = 128; *bn = 128; break;
+        case SCFG_R1C1_W4: *bm = 4; *bn = 64; break;
+        case SCFG_R4C1_W4: *bm = 16; *bn = 64; break;
+        case SCFG_R2C2_W4: *bm = 8; *bn = 128; break;
+        case SCFG_R8C1_W4: *bm = 32; *bn = 64; break;
+        case SCFG_R4C2_W8: *bm = 32; *bn = 128; break;
+        case SCFG_R8C2_W8: *bm = 64; *bn = 128; break;
         default: *bm = 64; *bn = 64; break;  // MCFG_64x64_W2
     }
 }
@@ -842,6 +1105,30 @@ int launch_mprod(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, Ou
         case M16CFG_128x64_W8: fn = Mprod16Table<2, 4, 1, 32>::get(lay_a, lay_b); threads = 512; break;
         case M16CFG_128x128_W8: fn = Mprod16Table<2, 4, 2, 16>::get(lay_a, lay_b); threads = 512; break;
         default: fn = MprodTable<1, 2, 1, 16, 2>::get(lay_a, lay_b); threads = 128; break;
+    }
+    hipLaunchKernelGGL(fn, grid, dim3(threads), 0, s, A, B, C, M, N, K,
+                       make_tile_grid(tiles_m, tiles_n, order));
+    return static_cast<int>(hipGetLastError());
+}
+
+int launch_srow(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, OutView C,
+                int64_t M, int64_t N, int64_t K, int64_t batch, int order, void* stream) {
+    int bm, bn;
+    tile_shape(cfg, &bm, &bn);
+    const int tiles_m = static_cast<int>((M + bm - 1) / bm);
+    const int tiles_n = static_cast<int>((N + bn - 1) / bn);
+    const dim3 grid(static_cast<unsigned>(tiles_m) * static_cast<unsigned>(tiles_n),
+                    static_cast<unsigned>(batch));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    TiledFn fn;
+    int threads;
+    switch (cfg) {
+        case SCFG_R1C1_W4: fn = SrowTable<1, 1, 4, 32>::get(lay_a, lay_b); threads = 256; break;
+        case SCFG_R2C2_W4: fn = SrowTable<2, 2, 4, 32>::get(lay_a, lay_b); threads = 256; break;
+        case SCFG_R8C1_W4: fn = SrowTable<8, 1, 4, 32>::get(lay_a, lay_b); threads = 256; break;
+        case SCFG_R4C2_W8: fn = SrowTable<4, 2, 8, 32>::get(lay_a, lay_b); threads = 512; break;
+        case SCFG_R8C2_W8: fn = SrowTable<8, 2, 8, 32>::get(lay_a, lay_b); threads = 512; break;
+        default: fn = SrowTable<4, 1, 4, 32>::get(lay_a, lay_b); threads = 256; break;
     }
     hipLaunchKernelGGL(fn, grid, dim3(threads), 0, s, A, B, C, M, N, K,
                        make_tile_grid(tiles_m, tiles_n, order));
