@@ -25,8 +25,10 @@ from ._lib import (  # noqa: F401
     REPOPS_ERR_NULL,
     REPOPS_ERR_STRIDE,
     REPOPS_ERR_VARIANT,
+    REPOPS_ERR_SCRATCH,
     REPOPS_ERR_WORKSPACE,
     REPOPS_MERKLE_DEFAULT_LEAF_BYTES,
+    REPOPS_NOALLOC_SCRATCH_BYTES,
     REPOPS_OK,
     RepopsError,
     load,
@@ -41,6 +43,7 @@ from ._lib import (  # noqa: F401
     repops_matmul_f32,
     repops_matmul_f32_ex,
     repops_merkle_root,
+    repops_merkle_root_noalloc,
     repops_merkle_workspace_bytes,
     repops_pick_variant_f32,
     repops_referee_matmul_f32,

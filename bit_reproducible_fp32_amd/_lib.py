@@ -22,6 +22,8 @@ REPOPS_ERR_HIP = 6
 REPOPS_ERR_DUPLICATE = 7
 REPOPS_ERR_ALIGN = 8
 REPOPS_ERR_WORKSPACE = 9
+REPOPS_ERR_SCRATCH = 10
+REPOPS_NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
 REPOPS_FOLD_MAX_PER_PASS = 64
 REPOPS_MERKLE_DEFAULT_LEAF_BYTES = 1024
 
@@ -39,6 +41,7 @@ EXPORTS = (
     "repops_fold_mean_sgd_f32",
     "repops_merkle_workspace_bytes",
     "repops_merkle_root",
+    "repops_merkle_root_noalloc",
     "repops_referee_matmul_f32",
     "repops_erf_f32",
     "repops_gelu_f32",
@@ -94,6 +97,8 @@ def load():
     lib.repops_merkle_workspace_bytes.restype = i64
     lib.repops_merkle_root.argtypes = [vp, i64, i64, vp, i64, vp, vp]
     lib.repops_merkle_root.restype = ci
+    lib.repops_merkle_root_noalloc.argtypes = [vp, i64, i64, vp, vp]
+    lib.repops_merkle_root_noalloc.restype = ci
     lib.repops_referee_matmul_f32.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i64, i64, ci,
                                               ci, i64, vp, i64, vp, i64, vp, vp, vp]
     lib.repops_referee_matmul_f32.restype = ci
@@ -184,6 +189,10 @@ def repops_merkle_workspace_bytes(nbytes, leaf_bytes) -> int:
 def repops_merkle_root(data, nbytes, leaf_bytes, workspace, workspace_bytes, root, stream) -> int:
     return load().repops_merkle_root(data, int(nbytes), int(leaf_bytes), workspace,
                                      int(workspace_bytes), root, stream)
+
+
+def repops_merkle_root_noalloc(data, nbytes, leaf_bytes, root, stream) -> int:
+    return load().repops_merkle_root_noalloc(data, int(nbytes), int(leaf_bytes), root, stream)
 
 
 def repops_referee_matmul_f32(A, a_rs, a_cs, B, b_rs, b_cs, C, M, N, K, trans_a, trans_b,

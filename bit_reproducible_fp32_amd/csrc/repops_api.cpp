@@ -343,6 +343,8 @@ const char* repops_strerror(repops_status status) {
         case REPOPS_ERR_DUPLICATE: return "two contributors share one identity";
         case REPOPS_ERR_ALIGN: return "a pointer is not aligned as the call requires";
         case REPOPS_ERR_WORKSPACE: return "the workspace is missing or too small";
+        case REPOPS_ERR_SCRATCH:
+            return "the call needs more scratch than the library's static buffer holds";
     }
     return "unknown status";
 }

@@ -124,6 +124,11 @@ int launch_fold(const FoldArgs& G, int n, bool first, bool last, float* sum, flo
 int64_t merkle_workspace_bytes(int64_t n_leaves, int64_t leaf_words);
 int launch_merkle_root(const uint32_t* data, int64_t total_words, int64_t leaf_words, void* ws,
                        uint32_t* root, bool vec, void* stream);
+// Size of the static device scratch behind repops_merkle_root_noalloc, and
+// the current device's address of it (nullptr, with the HIP error in
+// *hip_error, when the lookup fails).
+constexpr int64_t kStaticScratchBytes = int64_t(16) << 20;
+void* static_scratch_device_ptr(int* hip_error);
 // match[c] = (claims[8c .. 8c+7] == root[0 .. 7]) for c < nclaims.
 int launch_merkle_match(const uint32_t* root, const uint32_t* claims, int64_t nclaims,
                         int32_t* match, void* stream);

@@ -33,7 +33,15 @@
 // Everything is 32-bit integer arithmetic; there is no floating point here.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "repops_internal.h"
+
+// Device scratch of the no-allocation tensor hash: the same two ping-pong
+// digest buffers the workspace argument holds otherwise.  One copy per GPU,
+// alive until the process ends.  In host code `scratch` is only a handle for
+// hipGetSymbolAddress; kernels receive the device address it returns.
+static __device__ __align__(256) unsigned char scratch[repops::kStaticScratchBytes];
 
 namespace repops {
 namespace {
@@ -414,6 +422,32 @@ int launch_merkle_match(const uint32_t* root, const uint32_t* claims, int64_t nc
     hipLaunchKernelGGL(repops_merkle_match_kernel, dim3(static_cast<unsigned>(ceil_div(nclaims, 256))),
                        dim3(256), 0, static_cast<hipStream_t>(stream), root, claims, nclaims, match);
     return static_cast<int>(hipGetLastError());
+}
+
+void* static_scratch_device_ptr(int* hip_error) {
+    // Looked up once per device, with that device current, and cached: each
+    // GPU holds its own copy of the array at its own address.
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* ptr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *hip_error = static_cast<int>(err != hipSuccess ? err : hipErrorInvalidDevice);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptr[dev] == nullptr) {
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess || p == nullptr) {
+            *hip_error = static_cast<int>(err != hipSuccess ? err : hipErrorInvalidSymbol);
+            return nullptr;
+        }
+        ptr[dev] = p;
+    }
+    *hip_error = 0;
+    return ptr[dev];
 }
 
 }  // namespace repops

@@ -76,6 +76,23 @@ repops_status repops_merkle_root(const void* data, int64_t nbytes, int64_t leaf_
     return launch_root(data, nbytes, leaf_bytes, workspace, root, stream);
 }
 
+repops_status repops_merkle_root_noalloc(const void* data, int64_t nbytes, int64_t leaf_bytes,
+                                         void* root, void* stream) {
+    static_assert(REPOPS_NOALLOC_SCRATCH_BYTES == kStaticScratchBytes, "one scratch size");
+    if (!sizes_ok(nbytes, leaf_bytes)) return REPOPS_ERR_DIM;
+    const int64_t need = workspace_for(nbytes, leaf_bytes);
+    if (need > kStaticScratchBytes) return REPOPS_ERR_SCRATCH;
+    void* ws = nullptr;
+    if (need > 0) {
+        int err = 0;
+        ws = static_scratch_device_ptr(&err);
+        if (ws == nullptr) return REPOPS_ERR_HIP;
+    }
+    const repops_status st = check_merkle(data, nbytes, leaf_bytes, ws, need, root);
+    if (st != REPOPS_OK) return st;
+    return launch_root(data, nbytes, leaf_bytes, ws, root, stream);
+}
+
 repops_status repops_referee_matmul_f32(const float* A, int64_t a_rs, int64_t a_cs, const float* B,
                                         int64_t b_rs, int64_t b_cs, float* C, int64_t M, int64_t N,
                                         int64_t K, int trans_a, int trans_b, int64_t leaf_bytes,

@@ -38,7 +38,9 @@
  * then nothing is written.  Launch failures are reported as REPOPS_ERR_HIP;
  * faults during execution surface at the caller's next synchronisation.
  * No entry point synchronises the stream.  The calls that need device scratch
- * (the tensor hash) take it from the caller as a workspace argument.
+ * (the tensor hash) take it from the caller as a workspace argument; one
+ * variant, repops_merkle_root_noalloc, uses a fixed static device buffer
+ * instead (the only global state, see there).
  */
 #ifndef REPOPS_H
 #define REPOPS_H
@@ -61,7 +63,9 @@ typedef enum repops_status {
     REPOPS_ERR_HIP = 6,     /* the HIP runtime reported an error at launch */
     REPOPS_ERR_DUPLICATE = 7, /* two contributors share one identity */
     REPOPS_ERR_ALIGN = 8,   /* a pointer is not aligned as the call requires */
-    REPOPS_ERR_WORKSPACE = 9 /* the workspace is NULL or smaller than required */
+    REPOPS_ERR_WORKSPACE = 9, /* the workspace is NULL or smaller than required */
+    REPOPS_ERR_SCRATCH = 10   /* the call needs more than the static scratch
+                                 (REPOPS_NOALLOC_SCRATCH_BYTES) holds */
 } repops_status;
 
 /*
@@ -251,6 +255,32 @@ int64_t repops_merkle_workspace_bytes(int64_t nbytes, int64_t leaf_bytes);
 repops_status repops_merkle_root(const void* data, int64_t nbytes, int64_t leaf_bytes,
                                  void* workspace, int64_t workspace_bytes, void* root,
                                  void* stream);
+
+/*
+ * Bytes of the static device scratch behind repops_merkle_root_noalloc.
+ */
+#define REPOPS_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * repops_merkle_root without a workspace argument.  The intermediate digests
+ * go to a static device array of REPOPS_NOALLOC_SCRATCH_BYTES (16 MiB) that
+ * the library holds on each GPU it runs on until the process ends; this call
+ * allocates nothing.  The result is the same root as repops_merkle_root's.
+ * data, nbytes, leaf_bytes, root, stream: as in repops_merkle_root.
+ * Limit: repops_merkle_workspace_bytes(nbytes, leaf_bytes) must be at most
+ * REPOPS_NOALLOC_SCRATCH_BYTES (in 1 KiB leaves, up to about 512 MiB of data),
+ * else REPOPS_ERR_SCRATCH and nothing is queued.  The device is the current
+ * one, which must be the stream's; its first call looks up that device's
+ * array address (REPOPS_ERR_HIP if that fails).  Every call on one GPU shares
+ * that GPU's array: calls whose queued work may overlap in time on one GPU
+ * (other streams, other host threads, other graphs) race and must be ordered
+ * by the caller, e.g. all on one stream.  Errors: those of repops_merkle_root,
+ * with REPOPS_ERR_SCRATCH in place of REPOPS_ERR_WORKSPACE.
+ */
+repops_status repops_merkle_root_noalloc(const void* data, int64_t nbytes, int64_t leaf_bytes,
+                                         void* root, void* stream);
 
 /*
  * The referee's decision on an output-hash dispute over a matmul: queue

@@ -40,7 +40,7 @@ int main(void) {
     for (v = 0; v < n; ++v) CHECK(repops_variant_name(v) && strlen(repops_variant_name(v)) > 0);
     CHECK(strcmp(repops_variant_name(n), "?") == 0);
     CHECK(strcmp(repops_variant_name(-1), "?") == 0);
-    for (v = REPOPS_OK; v <= REPOPS_ERR_WORKSPACE; ++v)
+    for (v = REPOPS_OK; v <= REPOPS_ERR_SCRATCH; ++v)
         CHECK(strlen(repops_strerror((repops_status)v)) > 0);
     CHECK(strstr(repops_build_manifest(), "gfx950") != NULL);
 
