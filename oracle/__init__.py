@@ -6,11 +6,12 @@ calls it, and it imports nothing from the GPU library: the two share no code.
 
 Three independent implementations of one definition (Verde and RepOps
 article, section 3.2 "RepOps design principles", item 2, the matrix
-multiplication example: ``sum = 0``; for k in a fixed order
-``sum = sum + A[i][k] * B[k][j]``; ``C[i][j] = sum``), read as: ascending k,
-the multiply and the add each rounded to binary32 round-to-nearest-even
-(the Zoo chain-soundness spec pins RNE and turns fused multiply-add off),
-gradual underflow, ``sum`` starting at +0.0:
+multiplication example): C(i, j) is the inner product of row i of op(A) and
+column j of op(B), accumulated term by term in one fixed k order from a
+running sum that starts at zero.  Read as: ascending k, the running sum
+starting at +0.0, each multiply and each add rounded on its own to binary32
+round-to-nearest-even (the Zoo chain-soundness spec pins RNE and turns fused
+multiply-add off), gradual underflow:
 
 * :func:`matmul_f32` / :func:`entries_f32` -- the plain C triple loop in
   ``repops_oracle.c`` (the oracle proper), built with gcc;

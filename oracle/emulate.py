@@ -1,7 +1,7 @@
 """Binary64 emulation of the fixed-order FP32 matmul -- TEST INFRASTRUCTURE ONLY.
 
 Each step of the definition (Verde and RepOps article, section 3.2, item 2:
-``sum = 0``; ascending k: ``sum = sum + a*b``) is done in binary64 and the
+a running sum from zero, one term per k in ascending order) is done in binary64 and the
 result rounded to binary32 by numpy's cast (round-to-nearest-even, gradual
 underflow).  The binary64 product of two binary32 values is exact, and a
 binary64 sum rounded again to binary32 equals the correctly rounded binary32

@@ -10,7 +10,7 @@ IEEE 754-2008 section 6.3: an exact zero sum is +0 under round-to-nearest
 unless both addends are -0; a product's sign is the XOR of the operand signs.
 
 The loop is the definition in the Verde and RepOps article (section 3.2,
-item 2): ``sum = 0``; for k ascending ``sum = sum + a*b``; ``C[i][j] = sum``,
+item 2): a running sum from zero, one product added per k in ascending order,
 with the multiply and the add rounded separately.  Intended for tiny shapes.
 """
 from __future__ import annotations

@@ -8,14 +8,14 @@
  * the GPU library.
  *
  * What it computes (Verde and RepOps article, section 3.2 "RepOps design
- * principles", item 2, the matrix-multiplication example):
+ * principles", item 2, the matrix-multiplication example): every output
+ * C(i, j) is the inner product of row i of op(A) and column j of op(B),
+ * accumulated one term at a time in ascending k and in no other order, from
+ * a running sum that starts at zero; the (i, j) themselves may be computed
+ * in any order.  In this file's notation, with x_k = op(A)(i, k) and
+ * y_k = op(B)(k, j):
  *
- *   for every (i, j), in any order:
- *       sum = +0
- *       for k = 0, 1, ..., K-1 (this order and no other):
- *           a = op(A)(i, k);  b = op(B)(k, j)
- *           sum = sum + a * b
- *       C(i, j) = sum
+ *     s_0 = +0,   s_{k+1} = RN(s_k + RN(x_k * y_k)),   C(i, j) = s_K
  *
  * Readings taken here where the pages are open:
  *   - the multiply and the add are two separately rounded binary32
@@ -26,7 +26,7 @@
  *   - IEEE-754 binary32 with gradual underflow (the RepOps article, section
  *     3.3, requires IEEE-754 compliant hardware), so no flush-to-zero and no
  *     denormals-are-zero;
- *   - "sum = 0" is +0.0f and the first product is added to it;
+ *   - the running sum starts at +0.0f and the first product is added to it;
  *   - op(A)(i,k) = A[i*a_rs + k*a_cs] when trans_a == 0, else
  *     A[k*a_rs + i*a_cs]; op(B)(k,j) likewise with trans_b.  Strides are in
  *     elements and describe the stored matrix (the article, section 3.1,
@@ -69,21 +69,6 @@ int repops_oracle_env_status(void)
     return bad;
 }
 
-/* One output element, exactly as the definition above reads. */
-static float dot_fixed_order(const float *A, int64_t a_rs, int64_t a_cs, int trans_a,
-                             const float *B, int64_t b_rs, int64_t b_cs, int trans_b,
-                             int64_t i, int64_t j, int64_t K)
-{
-    float sum = 0.0f;
-    for (int64_t k = 0; k < K; ++k) {
-        const float a = trans_a ? A[k * a_rs + i * a_cs] : A[i * a_rs + k * a_cs];
-        const float b = trans_b ? B[j * b_rs + k * b_cs] : B[k * b_rs + j * b_cs];
-        const float p = a * b;  /* binary32 multiply, rounded on its own */
-        sum = sum + p;          /* binary32 add, rounded on its own */
-    }
-    return sum;
-}
-
 typedef struct {
     const float *A;
     int64_t a_rs, a_cs;
@@ -99,20 +84,55 @@ typedef struct {
     int64_t lo, hi;
 } oracle_job;
 
-static void *run_rows(void *arg)
+/*
+ * s_K of the recurrence above for one output: x points at x_0 and x_k sits at
+ * x[k * xs]; likewise y_k at y[k * ys].  Each of the two statements in the
+ * loop body is one binary32 operation, rounded on its own (FP_CONTRACT is
+ * off and FLT_EVAL_METHOD is 0).
+ */
+static float fixed_order_entry(const float *x, int64_t xs, const float *y, int64_t ys,
+                               int64_t K)
+{
+    float s = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+        const float prod = x[k * xs] * y[k * ys]; /* RN(x_k * y_k) */
+        s = s + prod;                             /* RN(s_k + prod) */
+    }
+    return s;
+}
+
+/* Where row i of op(A) starts, and its step along k, in elements. */
+static const float *op_a_row(const oracle_job *t, int64_t i, int64_t *step)
+{
+    if (t->trans_a) { *step = t->a_rs; return t->A + i * t->a_cs; }
+    *step = t->a_cs; return t->A + i * t->a_rs;
+}
+
+/* Where column j of op(B) starts, and its step along k, in elements. */
+static const float *op_b_col(const oracle_job *t, int64_t j, int64_t *step)
+{
+    if (t->trans_b) { *step = t->b_cs; return t->B + j * t->b_rs; }
+    *step = t->b_rs; return t->B + j * t->b_cs;
+}
+
+static float entry_of(const oracle_job *t, int64_t i, int64_t j)
+{
+    int64_t xs, ys;
+    const float *x = op_a_row(t, i, &xs);
+    const float *y = op_b_col(t, j, &ys);
+    return fixed_order_entry(x, xs, y, ys, t->K);
+}
+
+/* A thread's share: rows [lo, hi) of C, or entries [lo, hi) in entries mode. */
+static void *work_range(void *arg)
 {
     const oracle_job *t = (const oracle_job *)arg;
     if (t->ii) {
-        for (int64_t e = t->lo; e < t->hi; ++e)
-            t->out[e] = dot_fixed_order(t->A, t->a_rs, t->a_cs, t->trans_a, t->B, t->b_rs,
-                                        t->b_cs, t->trans_b, t->ii[e], t->jj[e], t->K);
+        for (int64_t e = t->lo; e < t->hi; ++e) t->out[e] = entry_of(t, t->ii[e], t->jj[e]);
         return NULL;
     }
     for (int64_t i = t->lo; i < t->hi; ++i)
-        for (int64_t j = 0; j < t->N; ++j)
-            t->C[i * t->c_rs + j * t->c_cs] =
-                dot_fixed_order(t->A, t->a_rs, t->a_cs, t->trans_a, t->B, t->b_rs, t->b_cs,
-                                t->trans_b, i, j, t->K);
+        for (int64_t j = 0; j < t->N; ++j) t->C[i * t->c_rs + j * t->c_cs] = entry_of(t, i, j);
     return NULL;
 }
 
@@ -131,16 +151,16 @@ static int run_split(oracle_job base, int64_t total, int nthreads)
         jobs[t].hi = total * (t + 1) / nthreads;
     }
     for (int t = 1; t < nthreads; ++t) {
-        if (pthread_create(&tid[t], NULL, run_rows, &jobs[t]) != 0) {
+        if (pthread_create(&tid[t], NULL, work_range, &jobs[t]) != 0) {
             rc = -3;
             break;
         }
         ++started;
     }
-    run_rows(&jobs[0]);
+    work_range(&jobs[0]);
     for (int t = 1; t <= started; ++t) pthread_join(tid[t], NULL);
     if (rc != 0) { /* finish the parts whose threads did not start */
-        for (int t = started + 1; t < nthreads; ++t) run_rows(&jobs[t]);
+        for (int t = started + 1; t < nthreads; ++t) work_range(&jobs[t]);
     }
     return 0;
 }

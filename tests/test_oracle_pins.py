@@ -321,26 +321,30 @@ def test_k_permutation_changes_order_sensitive_results():
 SRC = os.path.join(os.path.dirname(oracle.__file__), "repops_oracle.c")
 
 MUTANTS = {
-    "fused_multiply_add": [("        const float p = a * b;  /* binary32 multiply, rounded on its own */\n"
-                            "        sum = sum + p;          /* binary32 add, rounded on its own */",
-                            "        sum = fmaf(a, b, sum);")],
+    "fused_multiply_add": [("        const float prod = x[k * xs] * y[k * ys]; /* RN(x_k * y_k) */\n"
+                            "        s = s + prod;                             /* RN(s_k + prod) */",
+                            "        s = fmaf(x[k * xs], y[k * ys], s);")],
     "reversed_k": [("for (int64_t k = 0; k < K; ++k) {", "for (int64_t k = K - 1; k >= 0; --k) {")],
     "first_product_init": [
-        ("    float sum = 0.0f;\n",
-         "    float sum = K > 0 ? (trans_a ? A[i * a_cs] : A[i * a_rs]) * "
-         "(trans_b ? B[j * b_rs] : B[j * b_cs]) : 0.0f;\n"),
+        ("    float s = 0.0f;\n", "    float s = K > 0 ? x[0] * y[0] : 0.0f;\n"),
         ("for (int64_t k = 0; k < K; ++k) {", "for (int64_t k = 1; k < K; ++k) {")],
-    "binary64_accumulate": [("        sum = sum + p;          /* binary32 add, rounded on its own */",
-                             "        sum = (float)((double)sum + (double)a * (double)b);")],
-    "split_k": [("    float sum = 0.0f;\n", "    float sum = 0.0f, half = 0.0f;\n"),
-                ("        const float p = a * b;",
-                 "        if (k == K / 2) { half = sum; sum = 0.0f; }\n        const float p = a * b;"),
-                ("    return sum;\n}", "    return half + sum;\n}")],
-    "flush_to_zero": [("    float sum = 0.0f;\n",
-                       "    _mm_setcsr(_mm_getcsr() | 0x8040u);\n    float sum = 0.0f;\n")],
-    "transposed_a_index": [("A[i * a_rs + k * a_cs]", "A[i * a_cs + k * a_rs]")],
+    "binary64_accumulate": [("        s = s + prod;                             /* RN(s_k + prod) */",
+                             "        s = (float)((double)s + (double)x[k * xs] * (double)y[k * ys]);")],
+    "split_k": [("    float s = 0.0f;\n", "    float s = 0.0f, half = 0.0f;\n"),
+                ("        const float prod = x[k * xs]",
+                 "        if (k == K / 2) { half = s; s = 0.0f; }\n        const float prod = x[k * xs]"),
+                ("    return s;\n}", "    return half + s;\n}")],
+    # (the planted flush-to-zero mode is undone on return, so it does not leak
+    # into later oracle calls on the same thread)
+    "flush_to_zero": [("    float s = 0.0f;\n",
+                       "    const unsigned csr0 = _mm_getcsr();\n"
+                       "    _mm_setcsr(csr0 | 0x8040u);\n    float s = 0.0f;\n"),
+                      ("    return s;\n}", "    _mm_setcsr(csr0);\n    return s;\n}")],
+    "transposed_a_index": [("    *step = t->a_cs; return t->A + i * t->a_rs;",
+                            "    *step = t->a_rs; return t->A + i * t->a_cs;")],
     "dropped_last_k": [("for (int64_t k = 0; k < K; ++k) {", "for (int64_t k = 0; k + 1 < K; ++k) {")],
-    "wrong_b_index": [("B[k * b_rs + j * b_cs]", "B[k * b_cs + j * b_rs]")],
+    "wrong_b_index": [("    *step = t->b_rs; return t->B + j * t->b_cs;",
+                       "    *step = t->b_cs; return t->B + j * t->b_rs;")],
 }
 
 
