@@ -430,6 +430,8 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="time only the chosen workload (not the other matmul configurations "
                          "and the VALU-only kernel)")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the amd-smi clock readings (for runs under a profiler)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -450,7 +452,7 @@ def main():
 
     # Started before anything touches the GPU (amd-smi runs in a helper
     # process), and read once now, while the GPU is idle.
-    clocks = ClockReader() if args.workload in inputs.WORKLOADS else None
+    clocks = ClockReader() if args.workload in inputs.WORKLOADS and not args.no_clock else None
     sclk_before = clocks.read() if clocks else None
 
     import torch
@@ -493,7 +495,8 @@ def main():
     # clock); the shader clock is sampled from sysfs during the timed launches.
     t = time_matmul(torch, rp, w, ga, gb, out, stream, vidx, args.warmup, args.steps)
     wall, k_avg = t["wall_s"], t["mean_ms"]
-    sclk_load, n_load = clock_under_load(torch, stream, t["step"], k_avg, clocks)
+    sclk_load, n_load = (clock_under_load(torch, stream, t["step"], k_avg, clocks)
+                         if clocks else (None, 0))
 
     # Bit-exactness gates (the oracle decides): every output through the
     # digest of the oracle's whole output (committed table), and sampled

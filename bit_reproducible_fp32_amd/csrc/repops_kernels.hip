@@ -76,8 +76,14 @@ struct TileStage {
     __device__ static void coords(int tid, int v, int& x, int& k) {
         const int f = tid + NT * v;
         if constexpr (LAY == LAY_KC) {         // 4 consecutive k of one row
-            x = f / (BK / 4);
-            k = (f % (BK / 4)) * 4;
+            // 16 consecutive lanes take 16 consecutive rows and the next 16
+            // the next group of 4 k: a wave's loads still cover 16 whole
+            // 64-byte row pieces, and each of its four k-major LDS stores
+            // (row pitch BX + 4 = 4 mod 32 words) hits 64 distinct banks.
+            static_assert(BX % 16 == 0, "rows come in groups of 16");
+            constexpr int KQ = BK / 4;         // groups of 4 k per row
+            x = (f & 15) + 16 * (f / (16 * KQ));
+            k = ((f >> 4) % KQ) * 4;
         } else if constexpr (LAY == LAY_XC) {  // 4 consecutive x of one k
             x = (f % (BX / 4)) * 4;
             k = f / (BX / 4);
