@@ -492,7 +492,7 @@ def main():
     log("variant %s" % vname)
 
     # Warm-up launches run right before the timed ones (an idle GPU drops its
-    # clock); the shader clock is sampled from sysfs during the timed launches.
+    # clock); the shader clock is read with amd-smi while more launches run.
     t = time_matmul(torch, rp, w, ga, gb, out, stream, vidx, args.warmup, args.steps)
     wall, k_avg = t["wall_s"], t["mean_ms"]
     sclk_load, n_load = (clock_under_load(torch, stream, t["step"], k_avg, clocks)
