@@ -273,19 +273,33 @@ class ClockReader:
         except OSError:
             self.proc = None
 
-    def read(self, timeout_s=60.0):
-        import select
+    def request(self):
+        """Ask for one reading (answered by poll())."""
         if self.proc is None or self.proc.poll() is not None:
-            return None
+            return False
         try:
             self.proc.stdin.write("\n")
             self.proc.stdin.flush()
+            return True
+        except (OSError, ValueError):
+            return False
+
+    def poll(self, timeout_s=0.0):
+        """The requested reading if it has arrived within timeout_s, else
+        None."""
+        import select
+        if self.proc is None:
+            return None
+        try:
             ready, _, _ = select.select([self.proc.stdout], [], [], timeout_s)
             if not ready:
                 return None
             return parse_gfx_clocks(self.proc.stdout.readline())
         except (OSError, ValueError):
             return None
+
+    def read(self, timeout_s=60.0):
+        return self.poll(timeout_s) if self.request() else None
 
     def close(self):
         if self.proc is None:
@@ -298,14 +312,39 @@ class ClockReader:
         self.proc = None
 
 
-def clock_under_load(torch, stream, step, ms_per_step, clocks, seconds=2.5):
-    """gfx clocks read while `step` launches keep the GPU busy for about
-    `seconds` (the launches are queued first, then amd-smi runs)."""
-    n = max(1, int(seconds * 1e3 / max(ms_per_step, 1e-3)))
+def clock_under_load(torch, stream, step, ms_per_step, clocks, busy_before_s=2.2,
+                     max_seconds=30.0):
+    """gfx clocks read while `step` launches keep the GPU busy: batches of
+    about 20 ms of launches are queued, at most two ahead of the GPU, for
+    busy_before_s before the reading is requested (amd-smi's clock figures
+    refresh about once a second, so an earlier reading can still show the
+    idle clock) and until it has come back."""
+    ms = max(ms_per_step, 1e-3)
+    batch = max(1, int(20.0 / ms))
     torch.cuda.synchronize()
-    for _ in range(n):
-        step()
-    reading = clocks.read()
+    n = 0
+    pending = []
+
+    def one_batch():
+        nonlocal n
+        for _ in range(batch):
+            step()
+            n += 1
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        pending.append(ev)
+        if len(pending) > 2:
+            pending.pop(0).synchronize()
+
+    t_busy = time.perf_counter()
+    while time.perf_counter() - t_busy < busy_before_s:
+        one_batch()
+    reading = None
+    if clocks.request():
+        t0 = time.perf_counter()
+        while reading is None and time.perf_counter() - t0 < max_seconds:
+            one_batch()
+            reading = clocks.poll(0.0)
     torch.cuda.synchronize()
     return reading, n
 
@@ -528,12 +567,16 @@ def main():
     achieved = flops / (k_avg * 1e-3) / 1e12
     log("wall %.3f ms/step, kernel avg %.3f ms (median %.3f): %.2f TFLOP/s"
         % (ms_per_step, k_avg, t["per_launch"]["median"], achieved))
-    # Shader clock: amd-smi before the GPU was touched, while about 2.5 s of
-    # this kernel's launches ran, and at the end.  The kernel's own bound at
+    # Shader clock: amd-smi before the GPU was touched, while this kernel's
+    # launches keep the GPU busy, and at the end.  The kernel's own bound at
     # that clock: 256 CUs x 128 separately rounded FP32 lane operations.
     sclk = {"amd_smi_idle_before_mhz": sclk_before, "amd_smi_under_load_mhz": sclk_load,
             "launches_during_reading": n_load}
-    if sclk_load:
+    if sclk_load and min(sclk_load) < 1000:
+        # amd-smi answered with an idle-level clock although launches were
+        # queued: no clock-adjusted figure from it.
+        sclk["note"] = "under-load reading below 1000 MHz; not used"
+    elif sclk_load:
         mean_mhz = float(np.mean(sclk_load))
         sclk["under_load_mean_mhz"] = round(mean_mhz, 1)
         sclk["clock_adjusted_peak_tflops"] = round(256 * 128 * mean_mhz * 1e6 / 1e12, 2)
@@ -930,7 +973,20 @@ def bench_ops(args, torch, rp, inputs, dev):
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (k_avg * 1e-3) / 1e9
 
+    # The stock device copy of the same x into y, timed the same way: what
+    # moving these bytes costs with no arithmetic at all.
+    copy_bytes = 8.0 * n
+
+    def copy_step():
+        yt.copy_(xt)
+
+    for _ in range(args.warmup):
+        copy_step()
+    _, copy_ms = timed_region(torch, stream, copy_step, args.steps)
+
     # Bit-exactness gate: the whole output against the oracle.
+    step()
+    torch.cuda.synchronize()
     got = yt.cpu().numpy()
     t0 = time.perf_counter()
     if w.op == "layernorm":
@@ -963,6 +1019,11 @@ def bench_ops(args, torch, rp, inputs, dev):
                      "traffic": traffic},
         "cpu_baseline": cpu, "bitexact": True,
         "kernel_ms": {"mean": round(k_avg, 5)},
+        "stock_copy": {"what": "torch device copy of x into y (%d bytes read and written)"
+                               % int(copy_bytes),
+                       "ms": round(copy_ms, 5),
+                       "gbs": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1),
+                       "kernel_time_over_copy_time": round(k_avg / copy_ms, 3)},
     }
     print(json.dumps(rec), flush=True)
 

@@ -58,6 +58,7 @@ const Variant kVariants[] = {
     {"srow_t32x64x32_r8c1_w4_col", KIND_SROW, SCFG_R8C1_W4, ORDER_COL},
     {"srow_t32x128x32_r4c2_w8_xcd", KIND_SROW, SCFG_R4C2_W8, ORDER_XCD_GROUP},
     {"srow_t64x128x32_r8c2_w8_xcd", KIND_SROW, SCFG_R8C2_W8, ORDER_XCD_GROUP},
+    {"mprod1_t128x128x32_w8_xcd", KIND_MPROD, MCFG_128x128_W8_P1_K32, ORDER_XCD_GROUP},
 };
 constexpr int kNumVariants = static_cast<int>(sizeof(kVariants) / sizeof(kVariants[0]));
 
@@ -203,14 +204,16 @@ int classify(const OperandView& v, int64_t K, int64_t batch) {
 }
 
 int pick(const Problem& p) {
-    static const int large = variant_index("mprod1_t128x128x16_w8_xcd");
+    static const int large = variant_index("mprod1_t128x128x32_w8_xcd");
     static const int medium = variant_index("srow_t32x128x32_r4c2_w8_xcd");
     static const int small = variant_index("srow_t16x64x32_r4c1_w4_xcd");
     static const int tiny = variant_index("srow_t4x64x32_r1c1_w4_row");
     const int64_t tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch;
     const int64_t outputs = p.M * p.N * p.batch;
     // 256 CUs.  128x128 product tiles from one per CU up (measured fastest
-    // from 2048 x 2048 outputs).  Below that the scalar-row kernels, with few
+    // from 2048 x 2048 outputs), 32-deep k-tiles (0.7-2 % faster than 16-deep
+    // on the transformer-shaped products: whole 128-byte lines per k-tile for
+    // operands stored along k, half as many barriers).  Below that the scalar-row kernels, with few
     // outputs per lane, still give every SIMD several waves: 8 outputs per
     // lane from 2^19 outputs (fastest at 1024 x 1024), 4 from 2^17, and one
     // below (fastest at 256 x 256).

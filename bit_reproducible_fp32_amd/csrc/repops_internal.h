@@ -67,6 +67,9 @@ enum TileCfg : int {
     SCFG_R8C1_W4 = 17,  // 32 x 64
     SCFG_R4C2_W8 = 18,  // 32 x 128
     SCFG_R8C2_W8 = 19,  // 64 x 128
+    // MCFG_128x128_W8_P1 with 32-deep k-tiles: a row stored along k gives
+    // whole 128-byte lines per k-tile (67.6 KB of LDS, two workgroups per CU).
+    MCFG_128x128_W8_P1_K32 = 20,
 };
 
 // Workgroup -> output-tile traversal orders (never change a bit).

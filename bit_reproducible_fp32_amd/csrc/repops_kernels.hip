@@ -1074,6 +1074,7 @@ void tile_shape(int cfg, int* bm, int* bn) {
         case MCFG_128x128_W8: *bm = 128; *bn = 128; break;
         case MCFG_256x128_W8: *bm = 256; *bn = 128; break;
         case MCFG_128x128_W8_P1: *bm = 128; *bn = 128; break;
+        case MCFG_128x128_W8_P1_K32: *bm = 128; *bn = 128; break;
         case MCFG_128x128_W4_P1: *bm = 128; *bn = 128; break;
         case MCFG_256x128_W8_P1: *bm = 256; *bn = 128; break;
         case M16CFG_128x128_W16: *bm = 128; *bn = 128; break;
@@ -1105,6 +1106,7 @@ int launch_mprod(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, Ou
         case MCFG_128x128_W8: fn = MprodTable<2, 4, 1, 16, 2>::get(lay_a, lay_b); threads = 512; break;
         case MCFG_256x128_W8: fn = MprodTable<4, 2, 2, 16, 2>::get(lay_a, lay_b); threads = 512; break;
         case MCFG_128x128_W8_P1: fn = MprodTable<2, 4, 1, 16, 1>::get(lay_a, lay_b); threads = 512; break;
+        case MCFG_128x128_W8_P1_K32: fn = MprodTable<2, 4, 1, 32, 1>::get(lay_a, lay_b); threads = 512; break;
         case MCFG_128x128_W4_P1: fn = MprodTable<2, 2, 2, 16, 1>::get(lay_a, lay_b); threads = 256; break;
         case MCFG_256x128_W8_P1: fn = MprodTable<4, 2, 2, 16, 1>::get(lay_a, lay_b); threads = 512; break;
         case M16CFG_128x128_W16: fn = Mprod16Table<2, 8, 1, 32>::get(lay_a, lay_b); threads = 1024; break;

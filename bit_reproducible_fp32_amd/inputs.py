@@ -273,6 +273,10 @@ OPS_WORKLOADS = {
         OpsWorkload("distilbert_layernorm", "layernorm", 32 * 512, 768, 8201, 1e-12,
                     "LayerNorm over DistilBERT hidden states, 16384 tokens x 768, x ~ N(0,1) "
                     "times 4 plus 0.5, gamma ~ 1 + N(0, 0.02), beta ~ N(0, 0.02), eps 1e-12"),
+        OpsWorkload("layernorm_h4096", "layernorm", 32 * 512, 4096, 8301, 1e-5,
+                    "LayerNorm over 16384 rows x 4096 (a 4096-wide hidden state, the width of "
+                    "the 8B-shaped products), x ~ N(0,1) times 4 plus 0.5, gamma ~ 1 + N(0, 0.02), "
+                    "beta ~ N(0, 0.02), eps 1e-5"),
     ]
 }
 

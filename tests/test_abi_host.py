@@ -343,7 +343,7 @@ def test_pick_uses_each_kernel_family_by_size():
     def pick(M, N, K):
         return names[rp.repops_pick_variant_f32(PA, K, 1, PB, N, 1, M, N, K, 0, 0)]
 
-    assert pick(2048, 2048, 64) == "mprod1_t128x128x16_w8_xcd"
+    assert pick(2048, 2048, 64) == "mprod1_t128x128x32_w8_xcd"
     assert pick(1024, 1024, 1024) == "srow_t32x128x32_r4c2_w8_xcd"
     assert pick(512, 256, 1024) == "srow_t16x64x32_r4c1_w4_xcd"
     assert pick(256, 256, 256) == "srow_t4x64x32_r1c1_w4_row"
