@@ -20,10 +20,10 @@ JSON line on stdout; progress goes to stderr.
 * ``kernel_ms``: that mean, plus the median, min and max of a second pass
   with one event pair per launch.
 * ``sclk_mhz``: the gfx clock of each XCD from amd-smi (run by a helper
-  process started before the GPU was touched): idle before, while about
-  2.5 s of the timed kernel's launches run, and after; with the
-  clock-adjusted peak 256 x 128 x SCLK under load and the fraction of it
-  reached.
+  process started before the GPU was touched): idle before, after 2.2 s of
+  the timed kernel's launches with more still queued (amd-smi's figures
+  refresh about once a second), and after; with the clock-adjusted peak
+  256 x 128 x SCLK under load and the fraction of it reached.
 * ``bitexact_full``: the SHA-256 of the whole output equals the digest of the
   oracle's whole output (tests/golden/full_output_sha256.txt, written by a
   script that calls only the oracle); ``bitexact_sampled``: sampled entries
@@ -33,7 +33,11 @@ JSON line on stdout; progress goes to stderr.
   matrix instruction); ``configs``: every other matmul workload, each with
   its median time, roofline fraction, full-output bit-exactness and overhead
   against the stock FP32 GEMM (plus the oracle's single-thread time for the
-  two small ones).
+  two small ones); ``other_workloads``: the attention-shaped batched
+  products, the gradient fold, the tensor hash and ERF, GeLU and LayerNorm
+  (H = 768 and 4096), each timed and checked against the oracle as in its
+  own ``--workload`` mode (LayerNorm and erf/GeLU beside a device copy of the
+  same bytes).
 * ``cpu_baseline``: the CPU oracle (plain triple loop) timed on a bounded
   sample of the same workload -- the first R rows of C, all N columns, full
   K -- on this host's cores (within the CPU share OMP_NUM_THREADS states).
@@ -445,6 +449,27 @@ def run_config(torch, rp, inputs, name, dev, stream, variant=None, steps=20, war
     return rec
 
 
+# The other operators' workloads the default run also measures: the
+# attention-shaped batched products, the gradient fold, the tensor hash and
+# ERF, GeLU and LayerNorm.
+OTHER_WORKLOADS = ("llama8b_attn_scores", "llama8b_attn_pv", "fold_k8_d64M",
+                   "merkle_llama8b_mlp_up_C", "distilbert_gelu", "distilbert_erf",
+                   "distilbert_layernorm", "layernorm_h4096")
+
+
+def other_bench(name, inputs):
+    """The bench function of a non-matmul workload, or None."""
+    if name in inputs.FOLD_WORKLOADS:
+        return bench_fold
+    if name in inputs.BATCHED_WORKLOADS:
+        return bench_batched
+    if name in inputs.HASH_WORKLOADS:
+        return bench_merkle
+    if name in inputs.OPS_WORKLOADS:
+        return bench_ops
+    return None
+
+
 def main():
     from bit_reproducible_fp32_amd import inputs
 
@@ -469,6 +494,8 @@ def main():
     ap.add_argument("--no-configs", action="store_true",
                     help="time only the chosen workload (not the other matmul configurations "
                          "and the VALU-only kernel)")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the other operators' workloads in the default matmul run")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the amd-smi clock readings (for runs under a profiler)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -502,14 +529,10 @@ def main():
         sys.exit(1)
     rp.load()  # raises if the HIP library is not built
     dev = torch.device("cuda:0")
-    if args.workload in inputs.FOLD_WORKLOADS:
-        return bench_fold(args, torch, rp, inputs, dev)
-    if args.workload in inputs.BATCHED_WORKLOADS:
-        return bench_batched(args, torch, rp, inputs, dev)
-    if args.workload in inputs.HASH_WORKLOADS:
-        return bench_merkle(args, torch, rp, inputs, dev)
-    if args.workload in inputs.OPS_WORKLOADS:
-        return bench_ops(args, torch, rp, inputs, dev)
+    other = other_bench(args.workload, inputs)
+    if other is not None:
+        print(json.dumps(other(args, torch, rp, inputs, dev)), flush=True)
+        return
     w = inputs.WORKLOADS[args.workload]
     log("workload %s: %s" % (w.name, w.description))
     A, B = inputs.make_operands(w.name)
@@ -630,6 +653,25 @@ def main():
                                        stock=not args.no_torch_sgemm)
             torch.cuda.empty_cache()
 
+    # Every other operator's workload, each in its own launch configuration
+    # and checked against the oracle as in its own mode.
+    others = None
+    if not args.no_configs and args.variant is None and not args.no_others:
+        others = {}
+        for name in OTHER_WORKLOADS:
+            sub = argparse.Namespace(**vars(args))
+            # the same step counts as the workload's own mode
+            sub.workload, sub.steps, sub.warmup = name, 100, 200
+            sub.no_cpu_baseline, sub.calibrate_copy = True, False
+            r = other_bench(name, inputs)(sub, torch, rp, inputs, dev)
+            others[name] = {k: r[k] for k in ("metric", "value", "unit", "ms_per_step",
+                                              "kernel_ms", "roofline", "config") if k in r}
+            others[name]["bitexact"] = bool(r.get("bitexact", r.get("bitexact_sampled")))
+            for k in ("stock_copy", "referee"):
+                if k in r:
+                    others[name][k] = r[k]
+            torch.cuda.empty_cache()
+
     if args.calibrate_copy:
         calibration_copy(torch, dev)
     if clocks:
@@ -678,6 +720,8 @@ def main():
         rec["valu_only"] = valu
     if configs is not None:
         rec["configs"] = configs
+    if others is not None:
+        rec["other_workloads"] = others
     print(json.dumps(rec), flush=True)
 
 
@@ -740,7 +784,7 @@ def bench_batched(args, torch, rp, inputs, dev):
         "cpu_baseline": cpu, "bitexact_sampled": True,
         "kernel_ms": {"mean": round(k_avg, 4)},
     }
-    print(json.dumps(rec), flush=True)
+    return rec
 
 
 HBM_PEAK_GBS = 8000.0
@@ -809,7 +853,7 @@ def bench_fold(args, torch, rp, inputs, dev):
         "cpu_baseline": cpu, "bitexact_sampled": True,
         "kernel_ms": {"mean": round(k_avg, 5)},
     }
-    print(json.dumps(rec), flush=True)
+    return rec
 
 
 # ALU roofline of the tensor hash, in 32-bit VALU issue slots.  On gfx950 a
@@ -933,7 +977,7 @@ def bench_merkle(args, torch, rp, inputs, dev):
                     "hash_share_of_referee": round(k_avg / float(np.median(ref_ms)), 4),
                     "verdict_honest_vs_zero_claim": verdict},
     }
-    print(json.dumps(rec), flush=True)
+    return rec
 
 
 def bench_ops(args, torch, rp, inputs, dev):
@@ -1025,7 +1069,7 @@ def bench_ops(args, torch, rp, inputs, dev):
                        "gbs": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1),
                        "kernel_time_over_copy_time": round(k_avg / copy_ms, 3)},
     }
-    print(json.dumps(rec), flush=True)
+    return rec
 
 
 if __name__ == "__main__":

@@ -74,3 +74,11 @@ def test_gfx_clock_parsing(bench):
     assert bench.parse_gfx_clocks(text) == [2343, 2351]
     assert bench.parse_gfx_clocks("not json") is None
     assert bench.parse_gfx_clocks('{"gpu_data": []}') is None
+
+
+def test_other_workloads_name_known_workloads(bench):
+    """The default run's list of other operators' workloads names only
+    workloads that have a bench mode of their own."""
+    for name in bench.OTHER_WORKLOADS:
+        assert bench.other_bench(name, inputs) is not None, name
+    assert bench.other_bench("llama8b_mlp_up", inputs) is None
