@@ -209,16 +209,19 @@ int pick(const Problem& p) {
     static const int small = variant_index("srow_t16x64x32_r4c1_w4_xcd");
     static const int tiny = variant_index("srow_t4x64x32_r1c1_w4_row");
     const int64_t tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch;
+    const int64_t medium_tiles = ((p.M + 31) / 32) * ((p.N + 127) / 128) * p.batch;
     const int64_t outputs = p.M * p.N * p.batch;
     // 256 CUs.  128x128 product tiles from one per CU up (measured fastest
     // from 2048 x 2048 outputs), 32-deep k-tiles (0.7-2 % faster than 16-deep
     // on the transformer-shaped products: whole 128-byte lines per k-tile for
-    // operands stored along k, half as many barriers).  Below that the scalar-row kernels, with few
-    // outputs per lane, still give every SIMD several waves: 8 outputs per
-    // lane from 2^19 outputs (fastest at 1024 x 1024), 4 from 2^17, and one
-    // below (fastest at 256 x 256).
+    // operands stored along k, half as many barriers).  Below that the
+    // scalar-row kernels, with few outputs per lane, still give every SIMD
+    // several waves: 8 outputs per lane once their 32x128 tiles number one
+    // per CU (fastest from 1024 x 1024), 4 from 2^17 outputs (fastest at
+    // 768 x 768, where 32x128 tiles would leave CUs idle), and one below
+    // (fastest at 256 x 256).
     if (tiles >= 256) return large;
-    if (outputs >= (int64_t(1) << 19)) return medium;
+    if (medium_tiles >= 256) return medium;
     if (outputs >= (int64_t(1) << 17)) return small;
     return tiny;
 }

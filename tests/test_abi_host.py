@@ -335,9 +335,10 @@ def test_batched_injectivity_rule():
 
 def test_pick_uses_each_kernel_family_by_size():
     """The automatic choice: matrix-core products from 256 tiles of 128x128,
-    scalar-row kernels below (8 outputs per lane from 2^19 outputs, 4 from
-    2^17, one below), and the register-blocked VALU kernel instead of a
-    scalar-row one when K reaches 2^30 (their k offsets are 32-bit)."""
+    scalar-row kernels below (8 outputs per lane from 256 tiles of 32x128, 4
+    from 2^17 outputs, one below), and the register-blocked VALU kernel
+    instead of a scalar-row one when K reaches 2^30 (their k offsets are
+    32-bit)."""
     names = rp.variant_names()
 
     def pick(M, N, K):
@@ -346,6 +347,8 @@ def test_pick_uses_each_kernel_family_by_size():
     assert pick(2048, 2048, 64) == "mprod1_t128x128x32_w8_xcd"
     assert pick(1024, 1024, 1024) == "srow_t32x128x32_r4c2_w8_xcd"
     assert pick(512, 256, 1024) == "srow_t16x64x32_r4c1_w4_xcd"
+    assert pick(768, 768, 768) == "srow_t16x64x32_r4c1_w4_xcd"    # 144 tiles of 32x128
+    assert pick(2048, 1024, 1024) == "srow_t32x128x32_r4c2_w8_xcd"
     assert pick(256, 256, 256) == "srow_t4x64x32_r1c1_w4_row"
     assert pick(4, 4, (1 << 30) - 1) == "srow_t4x64x32_r1c1_w4_row"
     assert pick(4, 4, 1 << 30) == "valu_t64x64x16_r4x4_row"
