@@ -82,3 +82,69 @@ def test_other_workloads_name_known_workloads(bench):
     for name in bench.OTHER_WORKLOADS:
         assert bench.other_bench(name, inputs) is not None, name
     assert bench.other_bench("llama8b_mlp_up", inputs) is None
+
+
+class _FakeEvent:
+    def record(self, stream):
+        pass
+
+    def synchronize(self):
+        pass
+
+
+class _FakeCuda:
+    Event = _FakeEvent
+
+    @staticmethod
+    def synchronize():
+        pass
+
+
+class _FakeTorch:
+    cuda = _FakeCuda
+
+
+class _FakeClocks:
+    """Answers a request after `delay_polls` polls."""
+
+    def __init__(self, delay_polls, ok=True):
+        self.delay, self.ok, self.requested, self.polls = delay_polls, ok, None, 0
+
+    def request(self):
+        self.requested = self.polls
+        return self.ok
+
+    def poll(self, timeout_s=0.0):
+        self.polls += 1
+        if self.requested is not None and self.polls - self.requested > self.delay:
+            return [2300, 2310]
+        return None
+
+
+def test_clock_under_load_keeps_launching_until_the_reading(bench):
+    launches = []
+    clocks = _FakeClocks(delay_polls=5)
+    reading, n = bench.clock_under_load(_FakeTorch, None, lambda: launches.append(1), 10.0,
+                                        clocks, busy_before_s=0.0)
+    assert reading == [2300, 2310]
+    assert n == len(launches)
+    # batches of 20 ms / 10 ms per step = 2 launches, one per poll, until the
+    # sixth poll answers (no busy time asked for before the request)
+    assert n == 2 * 6
+
+
+def test_clock_under_load_busy_before_the_request(bench):
+    import time as _time
+    clocks = _FakeClocks(delay_polls=0)
+    t0 = _time.perf_counter()
+    reading, n = bench.clock_under_load(_FakeTorch, None, lambda: None, 10.0, clocks,
+                                        busy_before_s=0.05)
+    assert reading is not None and _time.perf_counter() - t0 >= 0.05
+    assert clocks.requested == 0      # nothing was polled before the request
+
+
+def test_clock_under_load_without_a_helper(bench):
+    clocks = _FakeClocks(delay_polls=0, ok=False)
+    reading, n = bench.clock_under_load(_FakeTorch, None, lambda: None, 10.0, clocks,
+                                        busy_before_s=0.0)
+    assert reading is None and n == 0
