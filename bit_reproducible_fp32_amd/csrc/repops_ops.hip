@@ -166,12 +166,13 @@ __device__ __forceinline__ float from_last(float s) {
 // FULL (every row of the wave live and exactly L * S long) drops every
 // bounds test, so that the loads are unconditional and issued in piece order,
 // and the sum can start on the first piece while later ones are in flight.
-template <int L, int S, bool VEC, bool FULL>
+template <int L, int S, bool VEC, bool FULL, class AfterLoads>
 __device__ __forceinline__ void ln_regs_group(const float* xs, float* ys, int hl, bool live,
                                               int64_t row, int seg, float fh, float eps,
                                               const float* gs, const float* bs,
                                               float* __restrict__ mean_out,
-                                              float* __restrict__ rstd_out) {
+                                              float* __restrict__ rstd_out,
+                                              AfterLoads after_loads) {
     constexpr int P = L == 4 ? 8 : 4;  // elements per piece
     constexpr int kPieces = S / P;
     constexpr int kStride = L * P;     // row offset from one piece of a lane to its next
@@ -194,6 +195,7 @@ __device__ __forceinline__ void ln_regs_group(const float* xs, float* ys, int hl
             v[i] = (FULL || o < hl) ? xs[o] : 0.0f;
         }
     }
+    after_loads();
 
     // S = ((+0 + x_0) + x_1) + ...
     float s = 0.0f;
@@ -286,21 +288,48 @@ __global__ __launch_bounds__(64) void repops_layernorm_regs_kernel(
     const int64_t groups = (rows + R - 1) / R;
     const float fh = static_cast<float>(H);
     const int hi = static_cast<int>(H);
-    if constexpr (VEC) {
-        for (int c = 4 * lane; c < L * S; c += 256) {
-            f32x4 gv = {1.0f, 1.0f, 1.0f, 1.0f}, bv = {-0.0f, -0.0f, -0.0f, -0.0f};
-            if (gamma && c < hi) gv = *reinterpret_cast<const f32x4*>(gamma + c);
-            if (beta && c < hi) bv = *reinterpret_cast<const f32x4*>(beta + c);
-            *reinterpret_cast<f32x4*>(ln_g + c) = gv;
-            *reinterpret_cast<f32x4*>(ln_b + c) = bv;
-        }
-    } else {
-        for (int c = lane; c < L * S; c += 64) {
-            ln_g[c] = gamma && c < hi ? gamma[c] : 1.0f;
-            ln_b[c] = beta && c < hi ? beta[c] : -0.0f;
+    // The staging loads are issued at once.  In the vector quad forms they
+    // are written to LDS only after the first row group's loads are in
+    // flight, so that their latency overlaps those loads instead of
+    // preceding them; the other forms write them at once (holding them
+    // across their loads would spill or cost occupancy).
+    constexpr bool kEarly = VEC && L == 4;
+    constexpr int kW = VEC ? 4 : 1;                        // floats per staging load
+    constexpr int kN = (L * S + 64 * kW - 1) / (64 * kW);  // staging loads per lane
+    f32x4 gv[kN], bv[kN];
+#pragma unroll
+    for (int q = 0; q < kN; ++q) {
+        const int c = kW * lane + 64 * kW * q;
+        gv[q] = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
+        bv[q] = f32x4{-0.0f, -0.0f, -0.0f, -0.0f};
+        if constexpr (VEC) {
+            if (c < L * S && gamma && c < hi) gv[q] = *reinterpret_cast<const f32x4*>(gamma + c);
+            if (c < L * S && beta && c < hi) bv[q] = *reinterpret_cast<const f32x4*>(beta + c);
+        } else {
+            if (c < L * S && gamma && c < hi) gv[q].x = gamma[c];
+            if (c < L * S && beta && c < hi) bv[q].x = beta[c];
         }
     }
-    __syncthreads();
+    bool staged = false;
+    auto stage = [&]() {
+        if (staged) return;
+#pragma unroll
+        for (int q = 0; q < kN; ++q) {
+            const int c = kW * lane + 64 * kW * q;
+            if (c < L * S) {
+                if constexpr (VEC) {
+                    *reinterpret_cast<f32x4*>(ln_g + c) = gv[q];
+                    *reinterpret_cast<f32x4*>(ln_b + c) = bv[q];
+                } else {
+                    ln_g[c] = gv[q].x;
+                    ln_b[c] = bv[q].x;
+                }
+            }
+        }
+        __syncthreads();
+        staged = true;
+    };
+    if constexpr (!kEarly) stage();
     for (int64_t rg = blockIdx.x; rg < groups; rg += gridDim.x) {
         const int64_t row = rg * R + lane / L;
         const bool live = row < rows;
@@ -312,10 +341,10 @@ __global__ __launch_bounds__(64) void repops_layernorm_regs_kernel(
         const bool full = (rg + 1) * R <= rows && hi == L * S;
         if (full)
             ln_regs_group<L, S, VEC, true>(xs, ys, hl, live, row, seg, fh, eps, ln_g + P * seg,
-                                           ln_b + P * seg, mean_out, rstd_out);
+                                           ln_b + P * seg, mean_out, rstd_out, stage);
         else
             ln_regs_group<L, S, VEC, false>(xs, ys, hl, live, row, seg, fh, eps, ln_g + P * seg,
-                                            ln_b + P * seg, mean_out, rstd_out);
+                                            ln_b + P * seg, mean_out, rstd_out, stage);
     }
 }
 
