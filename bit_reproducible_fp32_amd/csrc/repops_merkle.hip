@@ -91,6 +91,28 @@ __host__ __device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32
 #endif
 }
 
+// FIPS 180-4, section 4.1.2: Ch(e, f, g) takes f where e is set and g
+// elsewhere, Maj(a, b, c) the majority of the three bits.  Each is one
+// three-input logic op on the device, whose truth table is indexed by
+// 4 * first + 2 * second + third operand bit: 0xCA and 0xE8.  (Written as
+// plain expressions, Maj shares a ^ b and a & b between rounds and then
+// takes three instructions per round.)
+__host__ __device__ __forceinline__ uint32_t ch(uint32_t e, uint32_t f, uint32_t g) {
+#if __HIP_DEVICE_COMPILE__
+    return __builtin_amdgcn_bitop3_b32(e, f, g, 0xCA);
+#else
+    return (e & f) ^ (~e & g);
+#endif
+}
+
+__host__ __device__ __forceinline__ uint32_t maj(uint32_t a, uint32_t b, uint32_t c) {
+#if __HIP_DEVICE_COMPILE__
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0xE8);
+#else
+    return (a & b) ^ (a & c) ^ (b & c);
+#endif
+}
+
 __host__ __device__ __forceinline__ uint32_t bswap32(uint32_t x) { return __builtin_bswap32(x); }
 
 __host__ __device__ __forceinline__ void init_state(uint32_t (&h)[8]) {
@@ -115,11 +137,9 @@ __host__ __device__ __forceinline__ void compress(uint32_t (&h)[8], uint32_t (&w
             w[t & 15] = wt;
         }
         const uint32_t S1 = xor3(rotr(e, 6), rotr(e, 11), rotr(e, 25));
-        const uint32_t ch = (e & f) ^ (~e & g);
-        const uint32_t t1 = hh + S1 + ch + kRound[t] + wt;
+        const uint32_t t1 = hh + S1 + ch(e, f, g) + kRound[t] + wt;
         const uint32_t S0 = xor3(rotr(a, 2), rotr(a, 13), rotr(a, 22));
-        const uint32_t maj = (a & b) ^ (a & c) ^ (b & c);
-        const uint32_t t2 = S0 + maj;
+        const uint32_t t2 = S0 + maj(a, b, c);
         hh = g;
         g = f;
         f = e;
@@ -243,7 +263,7 @@ __host__ __device__ __forceinline__ void hash_node(const uint32_t (&l)[8], const
 constexpr int log2_of(int g) { return g <= 1 ? 0 : 1 + log2_of(g / 2); }
 
 template <int G, bool LEAF, bool VEC, bool FINAL>
-__global__ __launch_bounds__(G) void repops_merkle_kernel(const uint32_t* __restrict__ src,
+__global__ __launch_bounds__(G) __attribute__((amdgpu_waves_per_eu(4))) void repops_merkle_kernel(const uint32_t* __restrict__ src,
                                                           int64_t n_items, int64_t leaf_words,
                                                           int64_t total_words, int levels,
                                                           uint32_t* __restrict__ dst) {
