@@ -203,27 +203,50 @@ int classify(const OperandView& v, int64_t K, int64_t batch) {
     return LAY_GEN;
 }
 
+// The automatic choice.  Below 2^17 outputs the one-row scalar-row kernel.
+// Above, the candidate with the least estimated time, where the estimate is
+// the busiest CU's share of the work: with T tiles of BM x BN outputs over
+// 256 CUs, L = ceil(T / 256) tiles per CU, each at the family's measured
+// efficiency with L tiles queued on a CU (from a sweep of square and
+// rectangular products from 640 to 8192: a CU with one tile runs below its
+// steady rate, and tile counts just above a multiple of 256 leave CUs idle).
+// The 128 x 128 product kernel is kept unless another is estimated at least
+// 5 % faster: it is the measured best on every transformer-shaped product.
+// The choice never changes a bit.
+struct PickFamily {
+    const char* name;
+    int64_t bm, bn;
+    double eff[5];  // efficiency with 1, 2, 3, 4 and 5 or more tiles per CU
+};
+
+double pick_estimate(const PickFamily& f, const Problem& p) {
+    const int64_t tiles = ((p.M + f.bm - 1) / f.bm) * ((p.N + f.bn - 1) / f.bn) * p.batch;
+    const int64_t per_cu = (tiles + 255) / 256;
+    const double e = f.eff[per_cu < 5 ? per_cu - 1 : 4];
+    return static_cast<double>(per_cu) * static_cast<double>(f.bm * f.bn) / e;
+}
+
 int pick(const Problem& p) {
-    static const int large = variant_index("mprod1_t128x128x32_w8_xcd");
-    static const int medium = variant_index("srow_t32x128x32_r4c2_w8_xcd");
-    static const int small = variant_index("srow_t16x64x32_r4c1_w4_xcd");
+    static const PickFamily kLarge = {"mprod1_t128x128x32_w8_xcd", 128, 128,
+                                      {0.74, 0.84, 0.85, 0.87, 0.87}};
+    static const PickFamily kOthers[] = {
+        {"mprod16_t128x64x32_w8_xcd", 128, 64, {0.65, 0.73, 0.79, 0.83, 0.83}},
+        {"srow_t32x128x32_r4c2_w8_xcd", 32, 128, {0.49, 0.55, 0.60, 0.63, 0.63}},
+        {"srow_t16x64x32_r4c1_w4_xcd", 16, 64, {0.30, 0.38, 0.45, 0.48, 0.52}},
+    };
     static const int tiny = variant_index("srow_t4x64x32_r1c1_w4_row");
-    const int64_t tiles = ((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch;
-    const int64_t medium_tiles = ((p.M + 31) / 32) * ((p.N + 127) / 128) * p.batch;
-    const int64_t outputs = p.M * p.N * p.batch;
-    // 256 CUs.  128x128 product tiles from one per CU up (measured fastest
-    // from 2048 x 2048 outputs), 32-deep k-tiles (0.7-2 % faster than 16-deep
-    // on the transformer-shaped products: whole 128-byte lines per k-tile for
-    // operands stored along k, half as many barriers).  Below that the
-    // scalar-row kernels, with few outputs per lane, still give every SIMD
-    // several waves: 8 outputs per lane once their 32x128 tiles number one
-    // per CU (fastest from 1024 x 1024), 4 from 2^17 outputs (fastest at
-    // 768 x 768, where 32x128 tiles would leave CUs idle), and one below
-    // (fastest at 256 x 256).
-    if (tiles >= 256) return large;
-    if (medium_tiles >= 256) return medium;
-    if (outputs >= (int64_t(1) << 17)) return small;
-    return tiny;
+    static const int large_index = variant_index(kLarge.name);
+    static const int other_index[3] = {variant_index(kOthers[0].name),
+                                       variant_index(kOthers[1].name),
+                                       variant_index(kOthers[2].name)};
+    if (p.M * p.N * p.batch < (int64_t(1) << 17)) return tiny;
+    int best = 0;
+    double best_t = pick_estimate(kOthers[0], p);
+    for (int f = 1; f < 3; ++f) {
+        const double t = pick_estimate(kOthers[f], p);
+        if (t < best_t) best = f, best_t = t;
+    }
+    return best_t < 0.95 * pick_estimate(kLarge, p) ? other_index[best] : large_index;
 }
 
 // The scalar-row kernels count k, and A's byte offsets along k, in 32 bits;

@@ -334,21 +334,31 @@ def test_batched_injectivity_rule():
 
 
 def test_pick_uses_each_kernel_family_by_size():
-    """The automatic choice: matrix-core products from 256 tiles of 128x128,
-    scalar-row kernels below (8 outputs per lane from 256 tiles of 32x128, 4
-    from 2^17 outputs, one below), and the register-blocked VALU kernel
-    instead of a scalar-row one when K reaches 2^30 (their k offsets are
-    32-bit)."""
+    """The automatic choice: the one-row scalar-row kernel below 2^17
+    outputs; above, the family with the least estimated time for the busiest
+    CU (tiles per CU over the family's measured efficiency at that load), the
+    128x128 product kernel unless another is estimated 5 % faster; and the
+    register-blocked VALU kernel instead of a scalar-row one when K reaches
+    2^30 (their k offsets are 32-bit)."""
     names = rp.variant_names()
 
     def pick(M, N, K):
         return names[rp.repops_pick_variant_f32(PA, K, 1, PB, N, 1, M, N, K, 0, 0)]
 
-    assert pick(2048, 2048, 64) == "mprod1_t128x128x32_w8_xcd"
-    assert pick(1024, 1024, 1024) == "srow_t32x128x32_r4c2_w8_xcd"
-    assert pick(512, 256, 1024) == "srow_t16x64x32_r4c1_w4_xcd"
-    assert pick(768, 768, 768) == "srow_t16x64x32_r4c1_w4_xcd"    # 144 tiles of 32x128
-    assert pick(2048, 1024, 1024) == "srow_t32x128x32_r4c2_w8_xcd"
+    mp1, mp16 = "mprod1_t128x128x32_w8_xcd", "mprod16_t128x64x32_w8_xcd"
+    r4c2, r4c1 = "srow_t32x128x32_r4c2_w8_xcd", "srow_t16x64x32_r4c1_w4_xcd"
+    assert pick(4096, 14336, 4096) == mp1     # 3584 tiles of 128x128: 14 per CU
+    assert pick(4096, 2048, 8192) == mp1      # 512: two per CU
+    assert pick(2048, 2048, 64) == mp1        # 256: one per CU
+    assert pick(1792, 1792, 1792) == mp1      # 196
+    assert pick(2176, 2176, 2176) == mp16     # 289 of 128x128 would leave 223 CUs with one
+    assert pick(1408, 1408, 1408) == mp16     # 242 of 128x64, one per CU
+    assert pick(2048, 1024, 1024) == mp16     # 256 of 128x64
+    assert pick(1024, 1024, 1024) == r4c2     # 256 of 32x128
+    assert pick(1664, 1664, 1664) == r4c2     # 676 of 32x128: three per CU
+    assert pick(1152, 1152, 1152) == r4c1     # 324 of 32x128 would leave 188 CUs with one
+    assert pick(768, 768, 768) == r4c1        # 144 of 32x128
+    assert pick(512, 256, 1024) == r4c1       # 2^17 outputs
     assert pick(256, 256, 256) == "srow_t4x64x32_r1c1_w4_row"
     assert pick(4, 4, (1 << 30) - 1) == "srow_t4x64x32_r1c1_w4_row"
     assert pick(4, 4, 1 << 30) == "valu_t64x64x16_r4x4_row"
