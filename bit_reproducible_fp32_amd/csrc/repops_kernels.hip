@@ -393,7 +393,7 @@ __device__ __forceinline__ ConstF32Ptr uniform_ptr(ConstF32Ptr p) {
     return reinterpret_cast<ConstF32Ptr>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-template <int R, int CN, int W, int BK, int LA, int LB>
+template <int R, int CN, int W, int BK, int LA, int LB, bool PRIO>
 __global__ __launch_bounds__(64 * W) void repops_srow_kernel(OperandView A, OperandView B,
                                                              OutView C, int64_t M, int64_t N,
                                                              int64_t K, TileGrid grid) {
@@ -523,6 +523,7 @@ __global__ __launch_bounds__(64 * W) void repops_srow_kernel(OperandView A, Oper
             if (next) load_chunk(an);
             // Nothing moves across: the loads stay ahead of the arithmetic.
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int kk = 0; kk < AK; ++kk)
 #pragma unroll
@@ -535,6 +536,7 @@ __global__ __launch_bounds__(64 * W) void repops_srow_kernel(OperandView A, Oper
             for (int r = 0; r < R; ++r)
 #pragma unroll
                 for (int c = 0; c < CN; ++c) asm volatile("" : "+v"(acc[r][c]));
+            if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
             if (next) {
 #pragma unroll
                 for (int r = 0; r < R; ++r)
@@ -635,7 +637,7 @@ __device__ __forceinline__ int mprod_row(int v, int lane) {
 // of the SIMD to fill the wait, which halves the product registers and
 // raises occupancy.  The empty asm pins each step's adds before the next
 // step's LDS reads.
-template <int BK, int TN, int LDA, int LDB, int PIPE>
+template <int BK, int TN, int LDA, int LDB, int PIPE, bool PRIO>
 __device__ __forceinline__ void mprod_tile_steps(const float* as, const float* bs,
                                                  float (&acc)[TN][32]) {
     const f32x32 zero = {};
@@ -667,6 +669,7 @@ __device__ __forceinline__ void mprod_tile_steps(const float* as, const float* b
 #pragma unroll
                 for (int t = 0; t < TN; ++t) b[c][t] = bs[(k + 2) * LDB + t * 32];
             }
+            if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int t = 0; t < TN; ++t)
 #pragma unroll
@@ -675,6 +678,7 @@ __device__ __forceinline__ void mprod_tile_steps(const float* as, const float* b
             for (int t = 0; t < TN; ++t)
 #pragma unroll
                 for (int v = 0; v < 32; ++v) asm volatile("" : "+v"(acc[t][v]));
+            if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
             // Inside the step: matrix instructions, LDS reads, then the adds
             // (which read products issued one step earlier).
             __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
@@ -699,6 +703,7 @@ __device__ __forceinline__ void mprod_tile_steps(const float* as, const float* b
 #pragma unroll
                 for (int t = 0; t < TN; ++t) b[c ^ 1][t] = bs[(k + 1) * LDB + t * 32];
             }
+            if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int t = 0; t < TN; ++t)
 #pragma unroll
@@ -707,6 +712,7 @@ __device__ __forceinline__ void mprod_tile_steps(const float* as, const float* b
             for (int t = 0; t < TN; ++t)
 #pragma unroll
                 for (int v = 0; v < 32; ++v) asm volatile("" : "+v"(acc[t][v]));
+            if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
             __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1 + TN, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 32 * TN, 0);
@@ -727,7 +733,7 @@ __device__ __forceinline__ int mprod16_row(int v, int lane) {
     return 16 * (v >> 2) + 4 * (lane >> 4) + (v & 3);
 }
 
-template <int BK, int TN, int LDA, int LDB>
+template <int BK, int TN, int LDA, int LDB, bool PRIO>
 __device__ __forceinline__ void mprod16_tile_steps(const float* as, const float* bs,
                                                    float (&acc)[TN][16]) {
     const f32x16 zero = {};
@@ -747,6 +753,7 @@ __device__ __forceinline__ void mprod16_tile_steps(const float* as, const float*
 #pragma unroll
             for (int t = 0; t < TN; ++t) b[c ^ 1][t] = bs[(k + 1) * LDB + t * 16];
         }
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int t = 0; t < TN; ++t)
 #pragma unroll
@@ -755,6 +762,7 @@ __device__ __forceinline__ void mprod16_tile_steps(const float* as, const float*
         for (int t = 0; t < TN; ++t)
 #pragma unroll
             for (int v = 0; v < 16; ++v) asm volatile("" : "+v"(acc[t][v]));
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1 + TN, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 16 * TN, 0);
@@ -762,7 +770,7 @@ __device__ __forceinline__ void mprod16_tile_steps(const float* as, const float*
     }
 }
 
-template <int WAVES_M, int WAVES_N, int TN, int BK, int LA, int LB>
+template <int WAVES_M, int WAVES_N, int TN, int BK, int LA, int LB, bool PRIO>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void repops_mprod16_kernel(
     OperandView A, OperandView B, OutView C, int64_t M, int64_t N, int64_t K, TileGrid grid) {
     constexpr int NT = 64 * WAVES_M * WAVES_N;
@@ -824,7 +832,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void repops_mprod16_kernel(
         }
         asm volatile("" ::: "memory");
         const bool odd = (kt & 1) != 0;
-        mprod16_tile_steps<BK, TN, LDA, LDB>(odd ? as1 : as0, odd ? bs1 : bs0, acc);
+        mprod16_tile_steps<BK, TN, LDA, LDB, PRIO>(odd ? as1 : as0, odd ? bs1 : bs0, acc);
         asm volatile("" ::: "memory");
         if (more) {
             sa.store(odd ? As[0] : As[1], tid);
@@ -845,7 +853,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void repops_mprod16_kernel(
     }
 }
 
-template <int WAVES_M, int WAVES_N, int TN, int BK, int PIPE, int LA, int LB>
+template <int WAVES_M, int WAVES_N, int TN, int BK, int PIPE, int LA, int LB, bool PRIO>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void repops_mprod_kernel(
     OperandView A, OperandView B, OutView C, int64_t M, int64_t N, int64_t K, TileGrid grid) {
     constexpr int NT = 64 * WAVES_M * WAVES_N;
@@ -907,7 +915,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void repops_mprod_kernel(
         }
         asm volatile("" ::: "memory");
         const bool odd = (kt & 1) != 0;
-        mprod_tile_steps<BK, TN, LDA, LDB, PIPE>(odd ? as1 : as0, odd ? bs1 : bs0, acc);
+        mprod_tile_steps<BK, TN, LDA, LDB, PIPE, PRIO>(odd ? as1 : as0, odd ? bs1 : bs0, acc);
         asm volatile("" ::: "memory");
         if (more) {
             sa.store(odd ? As[0] : As[1], tid);
@@ -997,10 +1005,10 @@ struct CfgTable {
     }
 };
 
-template <int WM, int WN, int TN, int BK, int PIPE>
+template <int WM, int WN, int TN, int BK, int PIPE, bool PRIO = false>
 struct MprodTable {
     template <int LA, int LB>
-    static constexpr TiledFn fn() { return &repops_mprod_kernel<WM, WN, TN, BK, PIPE, LA, LB>; }
+    static constexpr TiledFn fn() { return &repops_mprod_kernel<WM, WN, TN, BK, PIPE, LA, LB, PRIO>; }
     static TiledFn get(int la, int lb) {
         static const TiledFn t[LAY_COUNT][LAY_COUNT] = {
             {fn<0, 0>(), fn<0, 1>(), fn<0, 2>()},
@@ -1011,10 +1019,10 @@ struct MprodTable {
     }
 };
 
-template <int WM, int WN, int TN, int BK>
+template <int WM, int WN, int TN, int BK, bool PRIO = false>
 struct Mprod16Table {
     template <int LA, int LB>
-    static constexpr TiledFn fn() { return &repops_mprod16_kernel<WM, WN, TN, BK, LA, LB>; }
+    static constexpr TiledFn fn() { return &repops_mprod16_kernel<WM, WN, TN, BK, LA, LB, PRIO>; }
     static TiledFn get(int la, int lb) {
         static const TiledFn t[LAY_COUNT][LAY_COUNT] = {
             {fn<0, 0>(), fn<0, 1>(), fn<0, 2>()},
@@ -1025,10 +1033,10 @@ struct Mprod16Table {
     }
 };
 
-template <int R, int CN, int W, int BK>
+template <int R, int CN, int W, int BK, bool PRIO = false>
 struct SrowTable {
     template <int LA, int LB>
-    static constexpr TiledFn fn() { return &repops_srow_kernel<R, CN, W, BK, LA, LB>; }
+    static constexpr TiledFn fn() { return &repops_srow_kernel<R, CN, W, BK, LA, LB, PRIO>; }
     static TiledFn get(int la, int lb) {
         static const TiledFn t[LAY_COUNT][LAY_COUNT] = {
             {fn<0, 0>(), fn<0, 1>(), fn<0, 2>()},
@@ -1090,6 +1098,9 @@ void tile_shape(int cfg, int* bm, int* bn) {
     }
 }
 
+// Tiles beyond which a launch uses the raised-priority kernel forms: one per CU.
+constexpr int64_t kPrioTiles = 256;
+
 int launch_mprod(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, OutView C,
                  int64_t M, int64_t N, int64_t K, int64_t batch, int order, void* stream) {
     int bm, bn;
@@ -1099,6 +1110,12 @@ int launch_mprod(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, Ou
     const dim3 grid(static_cast<unsigned>(tiles_m) * static_cast<unsigned>(tiles_n),
                     static_cast<unsigned>(batch));
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // With more tiles than CUs (several workgroups per CU), the kernels the
+    // automatic choice uses raise their waves' priority while they issue a
+    // step's adds (s_setprio 1), so that a wave that has its products goes
+    // on to its next matrix instruction or scalar loads sooner.  With one
+    // tile per CU or fewer the same hurt (measured), so it is off there.
+    const bool prio = static_cast<int64_t>(tiles_m) * tiles_n * batch > kPrioTiles;
     TiledFn fn;
     int threads;
     switch (cfg) {
@@ -1106,11 +1123,19 @@ int launch_mprod(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, Ou
         case MCFG_128x128_W8: fn = MprodTable<2, 4, 1, 16, 2>::get(lay_a, lay_b); threads = 512; break;
         case MCFG_256x128_W8: fn = MprodTable<4, 2, 2, 16, 2>::get(lay_a, lay_b); threads = 512; break;
         case MCFG_128x128_W8_P1: fn = MprodTable<2, 4, 1, 16, 1>::get(lay_a, lay_b); threads = 512; break;
-        case MCFG_128x128_W8_P1_K32: fn = MprodTable<2, 4, 1, 32, 1>::get(lay_a, lay_b); threads = 512; break;
+        case MCFG_128x128_W8_P1_K32:
+            fn = prio ? MprodTable<2, 4, 1, 32, 1, true>::get(lay_a, lay_b)
+                      : MprodTable<2, 4, 1, 32, 1>::get(lay_a, lay_b);
+            threads = 512;
+            break;
         case MCFG_128x128_W4_P1: fn = MprodTable<2, 2, 2, 16, 1>::get(lay_a, lay_b); threads = 256; break;
         case MCFG_256x128_W8_P1: fn = MprodTable<4, 2, 2, 16, 1>::get(lay_a, lay_b); threads = 512; break;
         case M16CFG_128x128_W16: fn = Mprod16Table<2, 8, 1, 32>::get(lay_a, lay_b); threads = 1024; break;
-        case M16CFG_128x64_W8: fn = Mprod16Table<2, 4, 1, 32>::get(lay_a, lay_b); threads = 512; break;
+        case M16CFG_128x64_W8:
+            fn = prio ? Mprod16Table<2, 4, 1, 32, true>::get(lay_a, lay_b)
+                      : Mprod16Table<2, 4, 1, 32>::get(lay_a, lay_b);
+            threads = 512;
+            break;
         case M16CFG_128x128_W8: fn = Mprod16Table<2, 4, 2, 16>::get(lay_a, lay_b); threads = 512; break;
         default: fn = MprodTable<1, 2, 1, 16, 2>::get(lay_a, lay_b); threads = 128; break;
     }
@@ -1128,15 +1153,25 @@ int launch_srow(int cfg, int lay_a, int lay_b, OperandView A, OperandView B, Out
     const dim3 grid(static_cast<unsigned>(tiles_m) * static_cast<unsigned>(tiles_n),
                     static_cast<unsigned>(batch));
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // Wave priority around the arithmetic, as in launch_mprod.
+    const bool prio = static_cast<int64_t>(tiles_m) * tiles_n * batch > kPrioTiles;
     TiledFn fn;
     int threads;
     switch (cfg) {
         case SCFG_R1C1_W4: fn = SrowTable<1, 1, 4, 32>::get(lay_a, lay_b); threads = 256; break;
         case SCFG_R2C2_W4: fn = SrowTable<2, 2, 4, 32>::get(lay_a, lay_b); threads = 256; break;
         case SCFG_R8C1_W4: fn = SrowTable<8, 1, 4, 32>::get(lay_a, lay_b); threads = 256; break;
-        case SCFG_R4C2_W8: fn = SrowTable<4, 2, 8, 32>::get(lay_a, lay_b); threads = 512; break;
+        case SCFG_R4C2_W8:
+            fn = prio ? SrowTable<4, 2, 8, 32, true>::get(lay_a, lay_b)
+                      : SrowTable<4, 2, 8, 32>::get(lay_a, lay_b);
+            threads = 512;
+            break;
         case SCFG_R8C2_W8: fn = SrowTable<8, 2, 8, 32>::get(lay_a, lay_b); threads = 512; break;
-        default: fn = SrowTable<4, 1, 4, 32>::get(lay_a, lay_b); threads = 256; break;
+        default:  // SCFG_R4C1_W4
+            fn = prio ? SrowTable<4, 1, 4, 32, true>::get(lay_a, lay_b)
+                      : SrowTable<4, 1, 4, 32>::get(lay_a, lay_b);
+            threads = 256;
+            break;
     }
     hipLaunchKernelGGL(fn, grid, dim3(threads), 0, s, A, B, C, M, N, K,
                        make_tile_grid(tiles_m, tiles_n, order));
