@@ -337,7 +337,7 @@ def test_pick_uses_each_kernel_family_by_size():
     """The automatic choice: the one-row scalar-row kernel below 2^17
     outputs; above, the family with the least estimated time for the busiest
     CU (tiles per CU over the family's measured efficiency at that load), the
-    128x128 product kernel unless another is estimated 5 % faster; and the
+    128x128 product kernel unless another is estimated 2 % faster; and the
     register-blocked VALU kernel instead of a scalar-row one when K reaches
     2^30 (their k offsets are 32-bit)."""
     names = rp.variant_names()
@@ -349,8 +349,9 @@ def test_pick_uses_each_kernel_family_by_size():
     r4c2, r4c1 = "srow_t32x128x32_r4c2_w8_xcd", "srow_t16x64x32_r4c1_w4_xcd"
     assert pick(4096, 14336, 4096) == mp1     # 3584 tiles of 128x128: 14 per CU
     assert pick(4096, 2048, 8192) == mp1      # 512: two per CU
-    assert pick(2048, 2048, 64) == mp1        # 256: one per CU
-    assert pick(1792, 1792, 1792) == mp1      # 196
+    assert pick(2688, 2688, 2688) == mp1      # 441: two per CU
+    assert pick(2048, 2048, 64) == mp16       # 512 of 128x64 (two per CU) against 256
+    assert pick(1792, 1792, 1792) == mp16     # 392 of 128x64 against 196
     assert pick(2176, 2176, 2176) == mp16     # 289 of 128x128 would leave 223 CUs with one
     assert pick(1408, 1408, 1408) == mp16     # 242 of 128x64, one per CU
     assert pick(2048, 1024, 1024) == mp16     # 256 of 128x64

@@ -28,7 +28,7 @@ CASES = [
     (768, 512, 128, False, True, "srow_t16x64x32_r4c1_w4_xcd"),     # 384 tiles of 16x64
     (1024, 1024, 256, True, False, "srow_t32x128x32_r4c2_w8_xcd"),  # 256 tiles of 32x128
     (2048, 1024, 256, False, False, "mprod16_t128x64x32_w8_xcd"),   # 256 tiles of 128x64
-    (2048, 2048, 128, False, True, "mprod1_t128x128x32_w8_xcd"),    # 256 tiles of 128x128
+    (4096, 2048, 64, False, True, "mprod1_t128x128x32_w8_xcd"),     # 512 tiles of 128x128
 ]
 
 
