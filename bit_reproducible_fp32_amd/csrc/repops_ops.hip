@@ -253,7 +253,14 @@ __device__ __forceinline__ void ln_regs_group(const float* xs, float* ys, int hl
                 t.w = v[4 * q + 3] * rs;
                 t = t * *reinterpret_cast<const f32x4*>(gs + o);
                 t = t + *reinterpret_cast<const f32x4*>(bs + o);
-                *reinterpret_cast<f32x4*>(ys + o) = t;
+                // 16 lanes write whole 256-byte runs of a row, which
+                // nontemporal stores pass on without keeping them; a quad's
+                // stores write half lines, which only plain stores let the
+                // cache merge
+                if constexpr (L == 16)
+                    __builtin_nontemporal_store(t, reinterpret_cast<f32x4*>(ys + o));
+                else
+                    *reinterpret_cast<f32x4*>(ys + o) = t;
             }
         }
     } else {
@@ -352,23 +359,36 @@ __global__ __launch_bounds__(64) void repops_layernorm_regs_kernel(
 // 16-lane register form, a row belongs to 16 consecutive lanes (4 rows per
 // one-wave workgroup) and round j deals elements [64 j, 64 j + 64) out in
 // pieces of 4 (lane g: 64 j + 4 g ...); the fixed-order sums walk the rounds
-// with the same ring step before every piece.  Here the row streams through
-// registers kRsChunk rounds at a time, three times: for the sum, for the sum
-// of squared deviations, and for the output.  Every load is issued
-// unconditionally (positions past H read the row's last piece and are then
-// replaced by +0), and the next chunk is loaded while the current one is
-// summed, so the sums follow the data in.
-constexpr int kRsChunk = 8;  // rounds per chunk
+// with the same ring step before every piece.  The row is read in chunks of
+// C rounds.  Its first NL chunks are kept in LDS and the next NR in
+// registers from the first pass on; the rest streams through two register
+// buffers three times (sum, sum of squared deviations, output), the next
+// chunk loaded while the current one is summed.  Every load is issued
+// unconditionally: a position past H reads the row's last piece and is then
+// replaced by +0, which leaves a running sum unchanged.  The output pass
+// takes the streamed chunks last to first (the ones the second pass read
+// last come first) and then the kept ones; y is written with nontemporal
+// stores, which keep the caches for x's second and third reads.
 
-// This lane's pieces of rounds j0 .. j0 + kRsChunk - 1 of the row at xr
-// (hi = H): element k of round j0 + q is a[4 q + k], +0 past H.
-template <bool VEC>
+// This lane's pieces of rounds j0 .. j0 + R - 1 of the row at xr (hi = H):
+// element k of round j0 + q is a[4 q + k], +0 past H.  IN: the rounds lie
+// inside the row, so no position needs the test.
+template <bool VEC, int R, bool IN = false>
 __device__ __forceinline__ void rs_load(const float* xr, int hi, int j0, int seg,
-                                        float (&a)[4 * kRsChunk]) {
+                                        float (&a)[4 * R]) {
 #pragma unroll
-    for (int q = 0; q < kRsChunk; ++q) {
+    for (int q = 0; q < R; ++q) {
         const int o = 64 * (j0 + q) + 4 * seg;
-        if constexpr (VEC) {
+        if constexpr (IN && VEC) {
+            const f32x4 t = *reinterpret_cast<const f32x4*>(xr + o);
+            a[4 * q] = t.x;
+            a[4 * q + 1] = t.y;
+            a[4 * q + 2] = t.z;
+            a[4 * q + 3] = t.w;
+        } else if constexpr (IN) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) a[4 * q + k] = xr[o + k];
+        } else if constexpr (VEC) {
             const bool in = o < hi;
             const f32x4 t = *reinterpret_cast<const f32x4*>(xr + (in ? o : hi - 4));
             a[4 * q] = in ? t.x : 0.0f;
@@ -386,11 +406,12 @@ __device__ __forceinline__ void rs_load(const float* xr, int hi, int j0, int seg
     }
 }
 
-// s runs on through one chunk: before each piece a ring step, then the
+// s runs on through R rounds: before each piece a ring step, then the
 // piece's 4 adds.
-__device__ __forceinline__ void rs_sum(float& s, const float (&a)[4 * kRsChunk]) {
+template <int R>
+__device__ __forceinline__ void rs_sum(float& s, const float (&a)[4 * R]) {
 #pragma unroll
-    for (int q = 0; q < kRsChunk; ++q) {
+    for (int q = 0; q < R; ++q) {
 #pragma unroll
         for (int g = 0; g < 16; ++g) {
             s = ring_step<16>(s);
@@ -400,16 +421,17 @@ __device__ __forceinline__ void rs_sum(float& s, const float (&a)[4 * kRsChunk])
     }
 }
 
-// The same over the squared deviations d = x - mu of one chunk (+0 past H).
-__device__ __forceinline__ void rs_sum_sq(float& s, const float (&a)[4 * kRsChunk], float mu,
-                                          int hi, int j0, int seg) {
+// The same over the squared deviations d = x - mu of R rounds (+0 past H).
+template <int R, bool IN = false>
+__device__ __forceinline__ void rs_sum_sq(float& s, const float (&a)[4 * R], float mu, int hi,
+                                          int j0, int seg) {
 #pragma unroll
-    for (int q = 0; q < kRsChunk; ++q) {
+    for (int q = 0; q < R; ++q) {
         float sq[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int e = 64 * (j0 + q) + 4 * seg + k;
-            const float d = e < hi ? a[4 * q + k] - mu : 0.0f;
+            const float d = (IN || e < hi) ? a[4 * q + k] - mu : 0.0f;
             sq[k] = d * d;
         }
 #pragma unroll
@@ -421,44 +443,174 @@ __device__ __forceinline__ void rs_sum_sq(float& s, const float (&a)[4 * kRsChun
     }
 }
 
-template <bool VEC>
+// y_i = ((x_i - mu) * rstd) * gamma_i + beta_i for R rounds from j0, with
+// gamma and beta loaded SPLIT parts at a time (a scheduling barrier before
+// each part keeps the compiler from loading them all at once).  A missing
+// gamma acts as 1 and a missing beta as -0 (t * 1 == t, t + (-0) == t).
+// Positions past H load the row's last piece and are never stored.
+template <bool VEC, int R, int SPLIT, bool IN = false>
+__device__ __forceinline__ void rs_out(const float (&c)[4 * R], int j0, int hi, int seg, bool live,
+                                       const float* xr, float* yr, const float* gamma,
+                                       const float* beta, float mu, float rs) {
+    const bool has_g = gamma != nullptr, has_b = beta != nullptr;
+    const float* gs = has_g ? gamma : xr;
+    const float* bs = has_b ? beta : xr;
+    constexpr int Q = R / SPLIT;
+#pragma unroll
+    for (int h = 0; h < SPLIT; ++h) {
+        if constexpr (SPLIT > 1) __builtin_amdgcn_sched_barrier(0);
+        float gv[4 * Q], bv[4 * Q];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int o = 64 * (j0 + h * Q + q) + 4 * seg;
+            if constexpr (VEC) {
+                const int oc = (IN || o < hi) ? o : hi - 4;
+                const f32x4 tg = *reinterpret_cast<const f32x4*>(gs + oc);
+                const f32x4 tb = *reinterpret_cast<const f32x4*>(bs + oc);
+                gv[4 * q] = tg.x;
+                gv[4 * q + 1] = tg.y;
+                gv[4 * q + 2] = tg.z;
+                gv[4 * q + 3] = tg.w;
+                bv[4 * q] = tb.x;
+                bv[4 * q + 1] = tb.y;
+                bv[4 * q + 2] = tb.z;
+                bv[4 * q + 3] = tb.w;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int ok = (IN || o + k < hi) ? o + k : hi - 1;
+                    gv[4 * q + k] = gs[ok];
+                    bv[4 * q + k] = bs[ok];
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            float t4[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float t = c[4 * (h * Q + q) + k] - mu;
+                t = t * rs;
+                t = t * (has_g ? gv[4 * q + k] : 1.0f);
+                t = t + (has_b ? bv[4 * q + k] : -0.0f);
+                t4[k] = t;
+            }
+            const int e0 = 64 * (j0 + h * Q + q) + 4 * seg;
+            if constexpr (VEC) {
+                // H is a multiple of 4 here, so e0 < H covers the whole float4
+                if (live && (IN || e0 < hi)) {
+                    const f32x4 w = {t4[0], t4[1], t4[2], t4[3]};
+                    __builtin_nontemporal_store(w, reinterpret_cast<f32x4*>(yr + e0));
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (live && (IN || e0 + k < hi)) yr[e0 + k] = t4[k];
+            }
+        }
+    }
+}
+
+// Rows up to this length take the form with more of the row kept on chip.
+constexpr int64_t kStreamKeepH = 4096;
+
+template <bool VEC, int C, int NL, int NR>
 __global__ __launch_bounds__(64) void repops_layernorm_stream_kernel(
     const float* x, int64_t x_rs, const float* __restrict__ gamma,
     const float* __restrict__ beta, float* y, int64_t y_rs, int64_t rows, int64_t H, float eps,
     float* __restrict__ mean_out, float* __restrict__ rstd_out) {
+    static_assert(NL >= 1 && NR >= 0 && C % 2 == 0, "kept chunks: at least one in LDS");
+    constexpr int K = NL + NR;  // kept chunks
+    // launched for rows longer than 2048 only, so the first KIN chunks lie
+    // inside every row and take no bounds tests
+    constexpr int KIN = 2048 / (64 * C);
+    // gamma and beta in half chunks for the short chunks, whole for long ones
+    constexpr int kOutSplit = C <= 4 ? 2 : 1;
+    __shared__ f32x4 kept[NL][C][64];
     const int lane = static_cast<int>(threadIdx.x);
     const int seg = lane & 15;
     const int hi = static_cast<int>(H);
     const float fh = static_cast<float>(H);
     const int rounds = (hi + 63) / 64;
     const int64_t groups = (rows + 3) / 4;
+    auto put = [&](int slot, const float (&c)[4 * C]) {
+#pragma unroll
+        for (int q = 0; q < C; ++q)
+            kept[slot][q][lane] = f32x4{c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]};
+    };
+    auto get = [&](int slot, float (&c)[4 * C]) {
+#pragma unroll
+        for (int q = 0; q < C; ++q) {
+            const f32x4 t = kept[slot][q][lane];
+            c[4 * q] = t.x;
+            c[4 * q + 1] = t.y;
+            c[4 * q + 2] = t.z;
+            c[4 * q + 3] = t.w;
+        }
+    };
     for (int64_t rg = blockIdx.x; rg < groups; rg += gridDim.x) {
         const int64_t row = rg * 4 + (lane >> 4);
         const bool live = row < rows;
         const float* xr = x + (live ? row : 0) * x_rs;
+        float sb[2][4 * C];                 // LDS staging, then the streamed chunks
+        float kr[NR > 0 ? NR : 1][4 * C];   // chunks NL .. K - 1
+        // where chunk c is loaded in the first pass (c is a constant in the
+        // unrolled loops below, so this resolves to one array)
+        auto home = [&](int c) -> float (&)[4 * C] {
+            return c < NL ? sb[c & 1] : (c < K ? kr[c - NL] : sb[0]);
+        };
 
-        // S = ((+0 + x_0) + x_1) + ..., a chunk loaded ahead of the one summed
-        float a[4 * kRsChunk], b[4 * kRsChunk];
+        // S = ((+0 + x_0) + x_1) + ...
         float s = 0.0f;
-        rs_load<VEC>(xr, hi, 0, seg, a);
-        for (int j = 0; j < rounds; j += 2 * kRsChunk) {
-            rs_load<VEC>(xr, hi, j + kRsChunk, seg, b);
-            rs_sum(s, a);
-            rs_load<VEC>(xr, hi, j + 2 * kRsChunk, seg, a);
-            rs_sum(s, b);
+        rs_load<VEC, C, true>(xr, hi, 0, seg, home(0));
+#pragma unroll
+        for (int c = 0; c < K; ++c) {
+            if (c + 1 < KIN)
+                rs_load<VEC, C, true>(xr, hi, (c + 1) * C, seg, home(c + 1));
+            else
+                rs_load<VEC, C>(xr, hi, (c + 1) * C, seg, home(c + 1));
+            if (c < NL) put(c, home(c));
+            rs_sum<C>(s, home(c));
         }
+        for (int j = K * C; j < rounds; j += 2 * C) {
+            rs_load<VEC, C>(xr, hi, j + C, seg, sb[1]);
+            rs_sum<C>(s, sb[0]);
+            if (j + C >= rounds) break;
+            rs_load<VEC, C>(xr, hi, j + 2 * C, seg, sb[0]);
+            rs_sum<C>(s, sb[1]);
+        }
+        // the chunks kept in LDS are read back from there, not carried in
+        // registers across the passes
+        asm volatile("" ::: "memory");
         s = __shfl(s, 15, 16);
         const float mu = s / fh;
 
         // S2 = sum of (x_i - mu) * (x_i - mu), the same way
         float s2 = 0.0f;
-        rs_load<VEC>(xr, hi, 0, seg, a);
-        for (int j = 0; j < rounds; j += 2 * kRsChunk) {
-            rs_load<VEC>(xr, hi, j + kRsChunk, seg, b);
-            rs_sum_sq(s2, a, mu, hi, j, seg);
-            rs_load<VEC>(xr, hi, j + 2 * kRsChunk, seg, a);
-            rs_sum_sq(s2, b, mu, hi, j + kRsChunk, seg);
+        rs_load<VEC, C>(xr, hi, K * C, seg, sb[0]);
+#pragma unroll
+        for (int c = 0; c < NL; ++c) {
+            get(c, sb[1]);
+            if (c < KIN)
+                rs_sum_sq<C, true>(s2, sb[1], mu, hi, c * C, seg);
+            else
+                rs_sum_sq<C>(s2, sb[1], mu, hi, c * C, seg);
         }
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            if (NL + r < KIN)
+                rs_sum_sq<C, true>(s2, kr[r], mu, hi, (NL + r) * C, seg);
+            else
+                rs_sum_sq<C>(s2, kr[r], mu, hi, (NL + r) * C, seg);
+        }
+        for (int j = K * C; j < rounds; j += 2 * C) {
+            rs_load<VEC, C>(xr, hi, j + C, seg, sb[1]);
+            rs_sum_sq<C>(s2, sb[0], mu, hi, j, seg);
+            if (j + C >= rounds) break;
+            rs_load<VEC, C>(xr, hi, j + 2 * C, seg, sb[0]);
+            rs_sum_sq<C>(s2, sb[1], mu, hi, j + C, seg);
+        }
+        asm volatile("" ::: "memory");
         s2 = __shfl(s2, 15, 16);
         const float var = s2 / fh;
         const float ve = var + eps;
@@ -469,27 +621,39 @@ __global__ __launch_bounds__(64) void repops_layernorm_stream_kernel(
             if (rstd_out) rstd_out[row] = rs;
         }
 
-        // y_i = ((x_i - mu) * rstd) * gamma_i + beta_i; a missing gamma acts
-        // as 1 and a missing beta as -0 (t * 1 == t, t + (-0) == t)
+        // the streamed chunks last to first, then the kept ones
         float* yr = y + (live ? row : 0) * y_rs;
-        const bool has_g = gamma != nullptr, has_b = beta != nullptr;
-        for (int j = 0; j < rounds; j += kRsChunk) {
-            float gv[4 * kRsChunk], bv[4 * kRsChunk];
-            rs_load<VEC>(xr, hi, j, seg, a);
-            rs_load<VEC>(has_g ? gamma : xr, hi, j, seg, gv);
-            rs_load<VEC>(has_b ? beta : xr, hi, j, seg, bv);
-#pragma unroll
-            for (int q = 0; q < kRsChunk; ++q) {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int e = 64 * (j + q) + 4 * seg + k;
-                    float t = a[4 * q + k] - mu;
-                    t = t * rs;
-                    t = t * (has_g ? gv[4 * q + k] : 1.0f);
-                    t = t + (has_b ? bv[4 * q + k] : -0.0f);
-                    if (live && e < hi) yr[e] = t;
-                }
+        const int nch = (rounds + C - 1) / C;
+        if (nch > K) {
+            rs_load<VEC, C>(xr, hi, (nch - 1) * C, seg, sb[0]);
+            for (int c = nch - 1; c >= K; c -= 2) {
+                if (c - 1 >= K) rs_load<VEC, C>(xr, hi, (c - 1) * C, seg, sb[1]);
+                rs_out<VEC, C, kOutSplit>(sb[0], c * C, hi, seg, live, xr, yr, gamma, beta, mu, rs);
+                if (c - 1 < K) break;
+                if (c - 2 >= K) rs_load<VEC, C>(xr, hi, (c - 2) * C, seg, sb[0]);
+                rs_out<VEC, C, kOutSplit>(sb[1], (c - 1) * C, hi, seg, live, xr, yr, gamma, beta, mu, rs);
             }
+        }
+#pragma unroll
+        for (int r = NR - 1; r >= 0; --r) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (NL + r < KIN)
+                rs_out<VEC, C, kOutSplit, true>(kr[r], (NL + r) * C, hi, seg, live, xr, yr,
+                                                gamma, beta, mu, rs);
+            else
+                rs_out<VEC, C, kOutSplit>(kr[r], (NL + r) * C, hi, seg, live, xr, yr, gamma,
+                                          beta, mu, rs);
+        }
+#pragma unroll
+        for (int c = NL - 1; c >= 0; --c) {
+            __builtin_amdgcn_sched_barrier(0);
+            get(c, sb[0]);
+            if (c < KIN)
+                rs_out<VEC, C, kOutSplit, true>(sb[0], c * C, hi, seg, live, xr, yr, gamma, beta,
+                                                mu, rs);
+            else
+                rs_out<VEC, C, kOutSplit>(sb[0], c * C, hi, seg, live, xr, yr, gamma, beta, mu,
+                                          rs);
         }
     }
 }
@@ -554,12 +718,17 @@ int launch_layernorm(const float* x, int64_t x_rs, const float* gamma, const flo
                            gamma, beta, y, y_rs, rows, H, eps, mean, rstd);
         return static_cast<int>(hipGetLastError());
     }
-    // Longer rows stream through registers, 16 lanes per row.
+    // Longer rows stream, 16 lanes per row.  Chunks of 4 rounds, 5 kept in
+    // LDS and 3 in registers (2048 elements of each row) up to 4096; above,
+    // chunks of 8 rounds with 2 kept in LDS; the unaligned (scalar-load) form
+    // uses the latter everywhere, as the former would spill there.
     const int64_t groups = (rows + 3) / 4;
     const int64_t blocks = groups < (int64_t(1) << 20) ? groups : (int64_t(1) << 20);
     using Fn = void (*)(const float*, int64_t, const float*, const float*, float*, int64_t,
                         int64_t, int64_t, float, float*, float*);
-    Fn fn = vec ? repops_layernorm_stream_kernel<true> : repops_layernorm_stream_kernel<false>;
+    Fn fn = !vec ? repops_layernorm_stream_kernel<false, 8, 2, 0>
+            : H <= kStreamKeepH ? repops_layernorm_stream_kernel<true, 4, 5, 5>
+                                : repops_layernorm_stream_kernel<true, 8, 2, 1>;
     hipLaunchKernelGGL(fn, dim3(static_cast<unsigned>(blocks)), dim3(64), 0, s, x, x_rs, gamma,
                        beta, y, y_rs, rows, H, eps, mean, rstd);
     return static_cast<int>(hipGetLastError());

@@ -174,6 +174,24 @@ def test_layernorm_shapes(rows, H):
     check_layernorm(x, g, None, 0.5)
 
 
+# Rows over 2048 keep their first chunks on chip: up to 4096 ten chunks of
+# 256 elements (five in LDS, five in registers; the first eight need no bounds
+# test), above that three of 512.  Lengths on both sides of each edge, with
+# partly filled row groups, in place, and through the scalar-load form (H odd).
+@pytest.mark.parametrize("rows,H", [(13, 2052), (6, 2300), (7, 2304), (9, 2308), (5, 2556),
+                                    (11, 2560), (6, 2564), (10, 4092), (7, 4100), (9, 4104),
+                                    (5, 4608), (6, 5124), (5, 2305), (6, 4099)])
+def test_layernorm_stream_kept_chunks(rows, H):
+    say("layernorm kept chunks rows=%d H=%d" % (rows, H))
+    rng = np.random.default_rng(rows * 7 + H)
+    x = (rng.standard_normal((rows, H)) * 3 + 1).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(H)).astype(np.float32)
+    b = (0.1 * rng.standard_normal(H)).astype(np.float32)
+    check_layernorm(x, g, b, 1e-5)
+    check_layernorm(x, None, b, 1e-6)
+    check_layernorm(x, g, b, 1e-5, in_place=True)
+
+
 @pytest.mark.parametrize("H,x_rs,offset", [(768, 772, 0), (768, 771, 0), (768, 768, 1),
                                           (768, 1000, 3), (1024, 1030, 0), (1024, 1027, 2),
                                           (2500, 2600, 0), (4096, 4100, 1), (6000, 6004, 0),
